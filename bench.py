@@ -1,0 +1,242 @@
+"""Benchmark of the sparse FP8 row-wise linear layer on one MI355X.
+
+A step is one forward pass of the layer over one batch: dynamic row-wise FP8
+quantization of the bf16 activation, then the 2:4 sparse FP8 GEMM with its
+fused scale/bias/bf16 epilogue.  The weight is prepared (row-wise FP8
+quantization + 2:4 compression) once, before timing, as a linear layer's
+weight is; its cost is timed separately and reported as ``weight_prep_ms``.
+
+Workload (headline): Llama-3.1-8B MLP up-projection at prefill,
+M=8192 tokens, K=4096, N=14336, e4m3 x e4m3, bf16 output, synthetic seeded
+inputs.  ``value`` is dense-equivalent TFLOP/s (2*M*N*K per step).  The
+decode-shaped secondary metric (GB/s at M in {1,4,16}, K=N=4096, bf16 bias)
+is reported under ``decode``; those calls rotate over enough distinct weight
+buffers (> 2x the 256 MB last-level cache) that every call reads HBM.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0          # dense FP8 MFMA, MI355X
+PEAK_FP8_SPARSE_TFLOPS = 10000.0  # 2:4 sparse FP8 MFMA (dense-equivalent), MI355X
+
+
+def gemm_bytes(m, n, k, bias, out_bytes=2):
+    """Algorithmic bytes of one linear call: compressed weight + metadata +
+    activation codes + scales (+ bias) + output."""
+    return n * k // 2 + n * k // 8 + m * k + 4 * m + 4 * n + (2 * n if bias else 0) + out_bytes * m * n
+
+
+def quant_bytes(m, k):
+    return 3 * m * k + 4 * m
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GB/s measurement")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=160, help="activation rows in the CPU oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer shards without communication along N; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sfr_inputs
+    import sparse_fp8_row_amd as sfr
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sfr.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    case = sfr_inputs.prefill_up_case()
+    M, N, K = case.m, case.n, case.k
+    x = to_dev(sfr_inputs.draw_x(case))
+    w = to_dev(sfr_inputs.draw_w(case))
+    print(f"[bench] {case.name}: inputs resident", file=sys.stderr, flush=True)
+
+    # weight preparation (once per weight), timed on its own
+    for _ in range(2):
+        pw = sfr.prepare_weight(w, torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = 5
+    for _ in range(reps):
+        pw = sfr.prepare_weight(w, torch.float8_e4m3fn)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prep_ms = e0.elapsed_time(e1) / reps
+
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    lib = sfr.load()
+    h = int(stream.cuda_stream)
+
+    def quant():
+        st = lib.quantize_rowwise_fp8(x.data_ptr(), M, K, sfr.SFR_E4M3, xq.data_ptr(), xs.data_ptr(), h)
+        assert st == 0, st
+
+    def gemm():
+        st = lib.sparse_fp8_rowwise_linear(xq.data_ptr(), sfr.SFR_E4M3, xs.data_ptr(), M, K, pw.values.data_ptr(),
+                                           pw.meta.data_ptr(), sfr.SFR_E4M3, pw.scale.data_ptr(), N, None,
+                                           out.data_ptr(), sfr.SFR_OUT_BF16, h)
+        assert st == 0, st
+
+    for _ in range(args.warmup):
+        quant()
+        gemm()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        quant()
+        evs[i][1].record(stream)
+        gemm()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    g_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
+    print(f"[bench] timed {args.steps} steps: step {step_ms:.4f} ms (quantize {q_ms:.4f}, gemm {g_ms:.4f}), "
+          f"host wall {wall * 1e3 / args.steps:.4f} ms/step", file=sys.stderr, flush=True)
+
+    flops = 2.0 * M * N * K
+    value = flops / (step_ms * 1e-3) / 1e12
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+    result = {
+        "metric": "sparse FP8 linear TFLOP/s (dense-equiv) @M=8192 K=4096 N=14336; GB/s @M=1..16",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic (seeded; Llama-3.1-8B up-proj shape)",
+        "config": {"workload": "prefill_up: quantize bf16 X[8192,4096] + 2:4 sparse FP8 linear N=14336, "
+                               "e4m3 x e4m3, bf16 out, no bias",
+                   "m": M, "n": N, "k": K, "x_dtype": "e4m3", "w_dtype": "e4m3", "out_dtype": "bf16",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "linear_tiled_kernel (256x256 tile)",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "frac_of_sparse_peak": round(gemm_tflops / PEAK_FP8_SPARSE_TFLOPS, 4),
+                     "traffic": None},
+        "kernels_ms": {"quantize": round(q_ms, 5), "gemm": round(g_ms, 5)},
+        "quantize_gbs": round(quant_bytes(M, K) / (q_ms * 1e-3) / 1e9, 1),
+        "weight_prep_ms": round(prep_ms, 4),
+    }
+    del xq, xs, out
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(torch, sfr, sfr_inputs, lib, dev, stream)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
+    """GEMM GB/s at M in {1,4,16}, K=N=4096, bf16 bias, rotating weights (> 512 MB)."""
+    res = {}
+    n, k = 4096, 4096
+    case0 = sfr_inputs.decode_cases()[0]
+    wb = sfr_inputs.draw_w(case0)
+    bb = sfr_inputs.draw_bias(case0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    w = to_dev(wb)
+    bias = to_dev(bb)
+    base = sfr.prepare_weight(w, torch.float8_e4m3fn)
+    per = n * k // 2 + n * k // 8
+    copies = int(np.ceil(600e6 / per))
+    vals = [base.values.clone() for _ in range(copies)]
+    metas = [base.meta.clone() for _ in range(copies)]
+    h = int(stream.cuda_stream)
+    for case in sfr_inputs.decode_cases():
+        m = case.m
+        x = to_dev(sfr_inputs.draw_x(case))
+        xq, xs = sfr.quantize_rowwise_fp8(x, torch.float8_e4m3fn)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        def call(i):
+            st = lib.sparse_fp8_rowwise_linear(xq.data_ptr(), sfr.SFR_E4M3, xs.data_ptr(), m, k,
+                                               vals[i].data_ptr(), metas[i].data_ptr(), sfr.SFR_E4M3,
+                                               base.scale.data_ptr(), n, bias.data_ptr(), out.data_ptr(),
+                                               sfr.SFR_OUT_BF16, h)
+            assert st == 0, st
+
+        for i in range(copies):
+            call(i)
+        torch.cuda.synchronize()
+        reps = 4 * copies
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i % copies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        b = gemm_bytes(m, n, k, True)
+        gbs = b / (us * 1e-6) / 1e9
+        res[f"M{m}"] = {"us_per_call": round(us, 3), "bytes": b, "GB/s": round(gbs, 1),
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        print(f"[bench] decode M={m}: {us:.3f} us/call, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+    return res
+
+
+def cpu_baseline(case, rows):
+    """The CPU oracle on a bounded sample of the same workload: quantize `rows`
+    activation rows, and evaluate the linear layer for those rows and all N
+    outputs (the weight's quantization and compression are not timed)."""
+    import oracle
+    import sfr_inputs
+    t_prep = time.perf_counter()
+    xb = sfr_inputs.draw_x(case)[:rows]
+    wb = sfr_inputs.draw_w(case)
+    wq, ws = oracle.quantize_rows(wb, oracle.E4M3)
+    v, m = oracle.compress_2to4(wq)
+    t_prep = time.perf_counter() - t_prep
+    t0 = time.perf_counter()
+    xq, xs = oracle.quantize_rows(xb, oracle.E4M3)
+    oracle.linear(xq, oracle.E4M3, xs, v, m, oracle.E4M3, ws)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.n * case.k
+    print(f"[bench] cpu oracle: {rows} rows in {dt:.2f} s", file=sys.stderr, flush=True)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {case.m} activation rows x all N={case.n} outputs, K={case.k} "
+                      f"(activation quantization + linear; {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

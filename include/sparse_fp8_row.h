@@ -1,0 +1,161 @@
+/*
+ * sparse_fp8_row.h -- C ABI of the MI355X (gfx950) row-wise-scaled FP8 linear
+ * layer with a 2:4 semi-structured sparse weight.
+ *
+ * The operation (pytorch/ao PR #1671, "Add CUTLASS-based row-wise scaled
+ * sparse FP8 kernel", ready-for-review comment, item 1: a converter of FP8
+ * data to a 2:4 sparse format, and a row-wise scaled linear operator for a
+ * sparse FP8 weight and an FP8 activation; item 4: the activation is quantized
+ * dynamically) is, with torch `linear` conventions (weight [N, K]):
+ *
+ *     out[m, n] = bf16( xs[m] * ws[n] * sum_k xq[m, k] * wq[n, k]  (+ bias[n]) )
+ *
+ * where xq/xs is the FP8 activation with one binary32 scale per row, wq/ws the
+ * FP8 weight with one binary32 scale per output row, and wq keeps at most two
+ * non-zeros in every group of four consecutive k.  Either operand may be OCP
+ * e4m3 ("fn": max 448, no infinities) or e5m2 (max 57344); the four dtype
+ * pairs are the four instantiations the pages list (pytorch/ao issue #3516,
+ * "Making torchao ABI compatible ...", file table).  A plain C ABI, free of
+ * any framework's C++ types, is the point that issue makes.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major data and
+ *    must be 16-byte aligned.  The caller owns all memory; the library never
+ *    allocates, frees or synchronizes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without waiting.  The library keeps no state
+ *    between calls and may be called from several host threads at once.
+ *  - Arguments are validated on the host before anything is launched.  On an
+ *    error nothing is launched and no output is touched.  Device faults (bad
+ *    pointers that pass validation) surface at the caller's next
+ *    synchronization, as usual in HIP.
+ *  - Outputs must not alias inputs.
+ *  - Inputs must be finite.  NaN or infinite inputs give unspecified results.
+ */
+#ifndef SPARSE_FP8_ROW_H
+#define SPARSE_FP8_ROW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* FP8 formats (OCP 8-bit floating point). */
+typedef enum { SFR_E4M3 = 0, SFR_E5M2 = 1 } sfr_fp8_t;
+
+/* Output formats of the linear layer.  SFR_OUT_F32 writes the binary32 value
+ * before the final bf16 rounding (for accuracy checks). */
+typedef enum { SFR_OUT_BF16 = 0, SFR_OUT_F32 = 1 } sfr_out_t;
+
+typedef enum {
+    SFR_OK = 0,
+    SFR_ERR_NULL = 1,   /* a required pointer is NULL                         */
+    SFR_ERR_SHAPE = 2,  /* a size is negative, too large or not a multiple    */
+    SFR_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                   */
+    SFR_ERR_DTYPE = 4,  /* an enum argument is out of range                   */
+    SFR_ERR_LAUNCH = 5  /* the HIP runtime rejected a kernel launch           */
+} sfr_status;
+
+/* Version of the compressed-weight layout described at compress_2to4_fp8. */
+#define SFR_FORMAT_VERSION 1
+
+/* Largest accepted row count / column count / K of any entry point. */
+#define SFR_MAX_DIM ((int64_t)1 << 30)
+
+/*
+ * quantize_rowwise_fp8 -- dynamic row-wise FP8 quantization.
+ * Source: PR #1671 (row-wise scaled FP8 activation, quantized dynamically;
+ * FP16->FP8 quantization must not produce NaN) and pytorch/ao PR #1455
+ * ("[float8nocompile] ... atomic_max-based algo ...", review thread: the split
+ * reduction is worth keeping because it is deterministic).
+ *
+ * For every row r of x (bf16 bits, [rows, cols]):
+ *     amax     = max_k |x[r, k]|                      (exact)
+ *     scale[r] = fl32(amax / fmax)                    (IEEE binary32 division;
+ *                                                      fmax 448 or 57344)
+ *     q[r, k]  = sat_rne_fp8(fl32(x[r, k] / scale[r]))
+ * sat_rne_fp8 rounds to nearest, ties to even, keeps the sign of zero, and
+ * clamps magnitudes above fmax to fmax.  A row whose amax is 0 gets
+ * scale 0 and codes 0x00 / 0x80 that keep each zero's sign.  The result is
+ * deterministic and exact: the same bytes on every run and every launch shape.
+ *
+ *   x      [rows, cols] bf16 bits, device, read.
+ *   dt     format of q.
+ *   q      [rows, cols] FP8 bytes, device, written.
+ *   scale  [rows] binary32, device, written.
+ * Sizes: 0 <= rows <= SFR_MAX_DIM, 0 < cols <= SFR_MAX_DIM, cols % 8 == 0.
+ * rows == 0 is a no-op; cols == 0 is rejected (SFR_ERR_SHAPE) because a row
+ * without elements has no amax.
+ */
+sfr_status quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt,
+                                uint8_t* q, float* scale, void* stream);
+
+/*
+ * compress_2to4_fp8 -- 2:4 semi-structured compression of an FP8 matrix.
+ * Source: PR #1671 (converter to the 2:4 sparse format; testing found that
+ * the compressor must treat -0.0 as zero, the issue the PR works around in
+ * `from_plain()` and fixes upstream).
+ *
+ * For every row n and every group g of four consecutive k (k = 4g .. 4g+3)
+ * of w ([n, k] FP8 bytes), the two entries of largest magnitude are kept;
+ * ties go to the lower index and +0 / -0 have equal (zero) magnitude.  With
+ * i0 < i1 the kept positions:
+ *     values[n, 2g]   = w[n, 4g + i0]     values[n, 2g+1] = w[n, 4g + i1]
+ *     (a kept -0.0, byte 0x80, is stored as 0x00)
+ *     meta[n, g / 2]  bits 4*(g%2) .. 4*(g%2)+3  =  i0 | (i1 << 2)
+ * so a little-endian 32-bit word of meta holds the nibbles of eight
+ * consecutive groups, even group in the low nibble (layout version
+ * SFR_FORMAT_VERSION).  Magnitude order is the unsigned order of the low
+ * seven bits, identical for e4m3 and e5m2; `dt` is validated and otherwise
+ * does not change the result.  Output is bit-exact and deterministic.
+ *
+ *   w      [n, k] FP8 bytes, device, read.
+ *   values [n, k/2] bytes, device, written.
+ *   meta   [n, k/8] bytes, device, written.
+ * Sizes: 0 <= n <= SFR_MAX_DIM, 0 < k <= SFR_MAX_DIM, k % 128 == 0.
+ * n == 0 is a no-op.
+ */
+sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t dt,
+                             uint8_t* values, uint8_t* meta, void* stream);
+
+/*
+ * sparse_fp8_rowwise_linear -- the row-wise scaled linear layer with a 2:4
+ * sparse FP8 weight.  Source: PR #1671 (row-wise scaled linear operator for a
+ * sparse FP8 weight and an FP8 activation, one instantiation per dtype pair,
+ * issue #3516's file table).
+ *
+ *     acc[m, n] = sum_k xq[m, k] * wq[n, k]          (binary32 accumulation of
+ *                                                    exact products, any order)
+ *     y[m, n]   = acc[m, n] * (xs[m] * ws[n]) (+ bias[n])   (binary32)
+ *     out[m, n] = bf16_rne(y[m, n])   or   y[m, n] with SFR_OUT_F32
+ * wq is the weight that (values, meta) encode in the compress_2to4_fp8
+ * layout.  Any accumulation order is a correct result; the library's order is
+ * fixed, so repeated calls give identical bits.
+ *
+ *   xq     [m, k] FP8 bytes (format x_dt), device, read.
+ *   xs     [m] binary32, device, read.
+ *   values [n, k/2], meta [n, k/8]: compressed weight (format w_dt), device, read.
+ *   ws     [n] binary32, device, read.
+ *   bias   [n] bf16 bits, device, read; may be NULL (no bias).
+ *   out    [m, n] bf16 bits (SFR_OUT_BF16) or binary32 (SFR_OUT_F32), device, written.
+ * Sizes: 0 <= m <= SFR_MAX_DIM, 0 <= n <= SFR_MAX_DIM, n % 16 == 0,
+ * 0 < k <= SFR_MAX_DIM, k % 128 == 0.  m == 0 or n == 0 is a no-op.
+ */
+sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs,
+                                     int64_t m, int64_t k,
+                                     const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                     const float* ws, int64_t n, const uint16_t* bias,
+                                     void* out, sfr_out_t out_dt, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sfr_status_string(sfr_status s);
+
+/* The compressed-weight layout version this library reads and writes. */
+int sfr_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FP8_ROW_H */

@@ -1,0 +1,168 @@
+"""Row-wise-scaled FP8 linear layer with a 2:4 sparse weight, for MI355X (gfx950).
+
+Thin Python binding of ``libsparse_fp8_row.so`` (C ABI in
+``include/sparse_fp8_row.h``).  This module only marshals arguments: every
+step of the computation runs in the library's HIP kernels.  PyTorch provides
+device memory and the current HIP stream.
+
+    xq, xs = quantize_rowwise_fp8(x)                    # x: bf16 [M, K] on the GPU
+    w = prepare_weight(w_bf16, torch.float8_e4m3fn)     # once per weight
+    y = sparse_fp8_rowwise_linear(xq, xs, w.values, w.meta, w.scale, bias)
+
+The operator follows pytorch/ao PR #1671 ("Add CUTLASS-based row-wise scaled
+sparse FP8 kernel"); see the header for the exact contract of each call.
+There is no fallback: if the library is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_fp8_row.so")
+
+SFR_E4M3, SFR_E5M2 = 0, 1
+SFR_OUT_BF16, SFR_OUT_F32 = 0, 1
+STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN",
+          4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
+EXPORTED = ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear",
+            "sfr_status_string", "sfr_format_version")
+
+_FP8 = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
+_lib = None
+
+
+class SfrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (torch is imported first so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m sparse_fp8_row_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.quantize_rowwise_fp8.argtypes = [P, I64, I64, I, P, P, P]
+    lib.compress_2to4_fp8.argtypes = [P, I64, I64, I, P, P, P]
+    lib.sparse_fp8_rowwise_linear.argtypes = [P, I, P, I64, I64, P, P, I, P, I64, P, P, I, P]
+    for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear):
+        fn.restype = I
+    lib.sfr_status_string.argtypes = [I]
+    lib.sfr_status_string.restype = ctypes.c_char_p
+    lib.sfr_format_version.argtypes = []
+    lib.sfr_format_version.restype = I
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SfrError(status, where)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fp8_enum(dtype) -> int:
+    if dtype not in _FP8:
+        raise ValueError(f"unsupported FP8 dtype {dtype}")
+    return _FP8[dtype]
+
+
+def quantize_rowwise_fp8(x: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None):
+    """bf16 [rows, cols] -> (q FP8 [rows, cols], scale float32 [rows])."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=dtype, device=x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(load().quantize_rowwise_fp8(x.data_ptr(), rows, cols, _fp8_enum(dtype), q.data_ptr(),
+                                       s.data_ptr(), _stream(stream)), "quantize_rowwise_fp8")
+    return q, s
+
+
+def compress_2to4_fp8(wq: torch.Tensor, stream=None):
+    """FP8 [n, k] -> (values FP8 [n, k/2], meta uint8 [n, k/8])."""
+    _dev(wq, "wq")
+    n, k = wq.shape
+    values = torch.empty((n, k // 2), dtype=wq.dtype, device=wq.device)
+    meta = torch.empty((n, k // 8), dtype=torch.uint8, device=wq.device)
+    _check(load().compress_2to4_fp8(wq.data_ptr(), n, k, _fp8_enum(wq.dtype), values.data_ptr(),
+                                    meta.data_ptr(), _stream(stream)), "compress_2to4_fp8")
+    return values, meta
+
+
+def sparse_fp8_rowwise_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.Tensor, meta: torch.Tensor,
+                              ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                              out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+    """out[m, n] = xs[m] * ws[n] * sum_k xq[m, k] * wq[n, k] (+ bias[n]), as bf16 (or float32)."""
+    for t, nm in ((xq, "xq"), (xs, "xs"), (values, "values"), (meta, "meta"), (ws, "ws")):
+        _dev(t, nm)
+    m, k = xq.shape
+    n = values.shape[0]
+    if values.shape != (n, k // 2) or meta.shape != (n, k // 8) or xs.shape != (m,) or ws.shape != (n,):
+        raise ValueError("operand shapes do not match")
+    if xs.dtype != torch.float32 or ws.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.shape != (n,):
+            raise ValueError("bias must be bfloat16 [n]")
+    od = {torch.bfloat16: SFR_OUT_BF16, torch.float32: SFR_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=xq.device)
+    elif out.shape != (m, n) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(load().sparse_fp8_rowwise_linear(
+        xq.data_ptr(), _fp8_enum(xq.dtype), xs.data_ptr(), m, k, values.data_ptr(), meta.data_ptr(),
+        _fp8_enum(values.dtype), ws.data_ptr(), n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od,
+        _stream(stream)), "sparse_fp8_rowwise_linear")
+    return out
+
+
+@dataclass
+class SparseFp8Weight:
+    """A prepared weight: 2:4-compressed FP8 values, metadata and row scales."""
+    values: torch.Tensor   # FP8 [N, K/2]
+    meta: torch.Tensor     # uint8 [N, K/8]
+    scale: torch.Tensor    # float32 [N]
+    format_version: int = 1
+
+
+def prepare_weight(w: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None) -> SparseFp8Weight:
+    """bf16 weight [N, K] -> row-wise FP8 quantization, then 2:4 compression.
+
+    The compressor keeps the two largest FP8 magnitudes of every group of four,
+    which is the 2:4 magnitude pruning; the row scale is unaffected by it because
+    a row's largest element is always kept."""
+    wq, ws = quantize_rowwise_fp8(w, dtype, stream)
+    values, meta = compress_2to4_fp8(wq, stream)
+    return SparseFp8Weight(values, meta, ws, int(load().sfr_format_version()))
+
+
+def linear(x: torch.Tensor, w: SparseFp8Weight, bias: Optional[torch.Tensor] = None,
+           act_dtype=torch.float8_e4m3fn, stream=None) -> torch.Tensor:
+    """bf16 x [M, K] -> bf16 [M, N]: dynamic activation quantization + sparse FP8 GEMM."""
+    xq, xs = quantize_rowwise_fp8(x, act_dtype, stream)
+    return sparse_fp8_rowwise_linear(xq, xs, w.values, w.meta, w.scale, bias, stream=stream)

@@ -1,0 +1,74 @@
+// C ABI of the sparse FP8 row-wise linear layer: argument validation and
+// dispatch to the gfx950 kernels.  The contract of every entry point is
+// documented in include/sparse_fp8_row.h.
+#include "sparse_fp8_row.h"
+
+#include "sfr_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool fp8_ok(int dt) { return dt == SFR_E4M3 || dt == SFR_E5M2; }
+// Bound on rows * cols of any one tensor, keeping every grid within HIP's limits.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+sfr_status launch_status(hipError_t e) { return e == hipSuccess ? SFR_OK : SFR_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+sfr_status quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt, uint8_t* q,
+                                float* scale, void* stream) {
+  if (!fp8_ok(dt)) return SFR_ERR_DTYPE;
+  if (rows < 0 || rows > SFR_MAX_DIM || cols <= 0 || cols > SFR_MAX_DIM || cols % 8 != 0 ||
+      rows * cols > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (rows == 0) return SFR_OK;
+  if (!x || !q || !scale) return SFR_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_quantize(x, rows, cols, dt, q, scale, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t dt, uint8_t* values, uint8_t* meta,
+                             void* stream) {
+  if (!fp8_ok(dt)) return SFR_ERR_DTYPE;
+  if (n < 0 || n > SFR_MAX_DIM || k <= 0 || k > SFR_MAX_DIM || k % 128 != 0 || n * k > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (n == 0) return SFR_OK;
+  if (!w || !values || !meta) return SFR_ERR_NULL;
+  if (!aligned16(w) || !aligned16(values) || !aligned16(meta)) return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_compress(w, n, k, values, meta, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs, int64_t m, int64_t k,
+                                     const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt, const float* ws,
+                                     int64_t n, const uint16_t* bias, void* out, sfr_out_t out_dt, void* stream) {
+  if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32)) return SFR_ERR_DTYPE;
+  if (m < 0 || m > SFR_MAX_DIM || n < 0 || n > SFR_MAX_DIM || n % 16 != 0 || k <= 0 || k > SFR_MAX_DIM ||
+      k % 128 != 0 || m * k > kMaxElems || n * k > kMaxElems || m * n > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (m == 0 || n == 0) return SFR_OK;
+  if (!xq || !xs || !values || !meta || !ws || !out) return SFR_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(values) || !aligned16(meta) || !aligned16(ws) ||
+      !aligned16(out) || (bias && !aligned16(bias)))
+    return SFR_ERR_ALIGN;
+  sfr::LinearArgs a{xq, xs, values, meta, ws, bias, out, m, n, k, (int)x_dt, (int)w_dt, (int)out_dt};
+  return launch_status(sfr::launch_linear(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* sfr_status_string(sfr_status s) {
+  switch (s) {
+    case SFR_OK: return "ok";
+    case SFR_ERR_NULL: return "null pointer";
+    case SFR_ERR_SHAPE: return "invalid shape";
+    case SFR_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SFR_ERR_DTYPE: return "invalid dtype";
+    case SFR_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int sfr_format_version(void) { return SFR_FORMAT_VERSION; }
+
+}  // extern "C"

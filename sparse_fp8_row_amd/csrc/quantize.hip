@@ -1,0 +1,152 @@
+// Row-wise dynamic FP8 quantization on gfx950.
+//
+// Method: pytorch/ao PR #1671 ("Add CUTLASS-based row-wise scaled sparse FP8
+// kernel"): FP8 activations with one scale per row, quantized dynamically, and
+// casts that never produce NaN.  The amax is a deterministic reduction, the
+// property the review of pytorch/ao PR #1455 ("[float8nocompile] ...
+// atomic_max-based algo ...") asks to keep; here it is an exact integer max
+// over the bf16 magnitude bits, reduced inside one wavefront, so no atomics
+// and no cross-workgroup step exist at all.
+//
+// Layout: one 64-lane wavefront owns one row.  Lane l holds 16-byte chunks
+// (8 bf16) l, l+64, l+128, ... of its row in registers between the amax sweep
+// and the cast sweep, so each input byte is read from HBM once.  Rows longer
+// than 32 chunks per lane (cols > 16384) take a two-sweep path that reads the
+// row again (from L2 in practice).
+#include "sfr_device.hpp"
+#include "sfr_launch.hpp"
+
+namespace sfr {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts of 64 lanes
+
+__device__ __forceinline__ uint32_t mag_max8(uint4 c, uint32_t m) {
+  // |bf16| order == unsigned order of the low 15 bits (finite inputs)
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7FFFu);
+    m = max(m, (w[i] >> 16) & 0x7FFFu);
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return m;
+}
+
+// 8 bf16 -> 8 FP8 bytes.  `scale` > 0: x / scale (IEEE binary32 division),
+// clamped to +/-fmax, rounded to nearest even by the hardware converter.
+template <int FMT>
+__device__ __forceinline__ uint2 cast8(uint4 c, float scale) {
+  constexpr float fmax = Fp8<FMT>::fmax;
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[2 * i] = bf16_to_f32(w[i] & 0xFFFFu) / scale;
+    t[2 * i + 1] = bf16_to_f32(w[i] >> 16) / scale;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(t[i], -fmax), fmax);
+  int lo = cvt_pk_fp8<FMT, false>(t[0], t[1], 0);
+  lo = cvt_pk_fp8<FMT, true>(t[2], t[3], lo);
+  int hi = cvt_pk_fp8<FMT, false>(t[4], t[5], 0);
+  hi = cvt_pk_fp8<FMT, true>(t[6], t[7], hi);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// All-zero row: keep each zero's sign (0x00 / 0x80).
+__device__ __forceinline__ uint2 zero8(uint4 c) {
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t b[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t s0 = (w[i] >> 15) & 1u, s1 = (w[i] >> 31) & 1u;
+    b[i / 2] |= ((s0 << 7) | (s1 << 15)) << (16 * (i % 2));
+  }
+  return make_uint2(b[0], b[1]);
+}
+
+template <int FMT, int R>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wavefront
+  const int64_t nchunks = cols >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+
+  if constexpr (R > 0) {
+    uint4 buf[R];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t c = lane + 64 * i;
+      buf[i] = c < nchunks ? xr[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) m = mag_max8(buf[i], m);
+    m = wave_max(m);
+    const float amax = bf16_to_f32(m);
+    const float s = amax / Fp8<FMT>::fmax;
+    if (lane == 0) scale[row] = (m == 0) ? 0.0f : s;
+    if (m == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t c = lane + 64 * i;
+        if (c < nchunks) qr[c] = zero8(buf[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t c = lane + 64 * i;
+        if (c < nchunks) qr[c] = cast8<FMT>(buf[i], s);
+      }
+    }
+  } else {
+    uint32_t m = 0;
+    for (int64_t c = lane; c < nchunks; c += 64) m = mag_max8(xr[c], m);
+    m = wave_max(m);
+    const float amax = bf16_to_f32(m);
+    const float s = amax / Fp8<FMT>::fmax;
+    if (lane == 0) scale[row] = (m == 0) ? 0.0f : s;
+    if (m == 0) {
+      for (int64_t c = lane; c < nchunks; c += 64) qr[c] = zero8(xr[c]);
+    } else {
+      for (int64_t c = lane; c < nchunks; c += 64) qr[c] = cast8<FMT>(xr[c], s);
+    }
+  }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                      hipStream_t stream) {
+  const int64_t per_lane = ((cols >> 3) + 63) / 64;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+#define SFR_Q(R) hipLaunchKernelGGL((quantize_rows_kernel<FMT, R>), grid, block, 0, stream, x, rows, cols, q, scale)
+  if (per_lane <= 1) SFR_Q(1);
+  else if (per_lane <= 2) SFR_Q(2);
+  else if (per_lane <= 4) SFR_Q(4);
+  else if (per_lane <= 8) SFR_Q(8);
+  else if (per_lane <= 16) SFR_Q(16);
+  else if (per_lane <= 32) SFR_Q(32);
+  else SFR_Q(0);
+#undef SFR_Q
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                           float* scale, hipStream_t stream) {
+  if (fmt == FMT_E4M3) return launch_fmt<FMT_E4M3>(x, rows, cols, q, scale, stream);
+  return launch_fmt<FMT_E5M2>(x, rows, cols, q, scale, stream);
+}
+
+}  // namespace sfr

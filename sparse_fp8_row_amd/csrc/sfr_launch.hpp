@@ -1,0 +1,30 @@
+// Host-side launchers of the gfx950 kernels (internal; the C ABI validates
+// arguments before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfr {
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                           float* scale, hipStream_t stream);
+
+hipError_t launch_compress(const uint8_t* w, int64_t n, int64_t k, uint8_t* values, uint8_t* meta,
+                           hipStream_t stream);
+
+struct LinearArgs {
+  const uint8_t* xq;
+  const float* xs;
+  const uint8_t* values;
+  const uint8_t* meta;
+  const float* ws;
+  const uint16_t* bias;  // may be null
+  void* out;
+  int64_t m, n, k;
+  int x_fmt, w_fmt, out_fmt;
+};
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace sfr

@@ -1,0 +1,108 @@
+"""The C ABI on the CPU: the built library loads, exports every function the
+header declares, and rejects invalid arguments with the documented status
+before anything is launched (so these calls need no GPU)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_fp8_row.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_fp8_row_amd as sfr
+    if not os.path.exists(sfr.LIB_PATH):
+        from sparse_fp8_row_amd import build
+        build.build()
+    return sfr.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
+              "sfr_format_version"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.sfr_format_version() == 1
+    assert lib.sfr_status_string(0) == b"ok"
+    assert lib.sfr_status_string(2) == b"invalid shape"
+    assert lib.sfr_status_string(99) == b"unknown status"
+
+
+OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+A = 0x10000          # a 16-byte aligned stand-in address (never dereferenced: every call below fails validation)
+U = 0x10001          # a misaligned one
+
+
+def test_quantize_validation(lib):
+    q = lib.quantize_rowwise_fp8
+    assert q(A, 4, 16, 2, A, A, None) == DTYPE
+    assert q(A, 4, 15, 0, A, A, None) == SHAPE          # cols % 8
+    assert q(A, 4, 0, 0, A, A, None) == SHAPE           # no elements
+    assert q(A, -1, 16, 0, A, A, None) == SHAPE
+    assert q(A, 4, (1 << 30) + 8, 0, A, A, None) == SHAPE
+    assert q(None, 0, 16, 0, None, None, None) == OK    # empty: no-op
+    assert q(None, 4, 16, 0, A, A, None) == NULL
+    assert q(A, 4, 16, 0, A, None, None) == NULL
+    assert q(U, 4, 16, 0, A, A, None) == ALIGN
+    assert q(A, 4, 16, 1, A, U, None) == ALIGN
+
+
+def test_compress_validation(lib):
+    c = lib.compress_2to4_fp8
+    assert c(A, 4, 128, -1, A, A, None) == DTYPE
+    assert c(A, 4, 64, 0, A, A, None) == SHAPE          # k % 128
+    assert c(A, 4, 0, 0, A, A, None) == SHAPE
+    assert c(A, -4, 128, 0, A, A, None) == SHAPE
+    assert c(None, 0, 128, 0, None, None, None) == OK
+    assert c(A, 4, 128, 0, None, A, None) == NULL
+    assert c(A, 4, 128, 0, A, U, None) == ALIGN
+
+
+def test_linear_validation(lib):
+    f = lib.sparse_fp8_rowwise_linear
+    good = dict(xq=A, xd=0, xs=A, m=4, k=256, v=A, meta=A, wd=0, ws=A, n=32, bias=None, out=A, od=0)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["xq"], a["xd"], a["xs"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["n"],
+                 a["bias"], a["out"], a["od"], None)
+
+    assert call(xd=2) == DTYPE
+    assert call(wd=5) == DTYPE
+    assert call(od=3) == DTYPE
+    assert call(k=192) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(n=24) == SHAPE
+    assert call(m=-1) == SHAPE
+    assert call(m=(1 << 30) + 1) == SHAPE
+    assert call(m=0, xq=None, xs=None, out=None) == OK
+    assert call(n=0, v=None, meta=None, ws=None) == OK
+    assert call(xq=None) == NULL
+    assert call(meta=None) == NULL
+    assert call(out=None) == NULL
+    assert call(ws=U) == ALIGN
+    assert call(bias=U) == ALIGN
+    assert call(out=U) == ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    import sparse_fp8_row_amd as sfr
+    with pytest.raises(ValueError):
+        sfr.quantize_rowwise_fp8(torch.zeros((2, 16), dtype=torch.bfloat16))
