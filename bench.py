@@ -46,8 +46,8 @@ def quant_bytes(m, k):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GB/s measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=160, help="activation rows in the CPU oracle sample")

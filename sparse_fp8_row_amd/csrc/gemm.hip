@@ -20,15 +20,19 @@
 // Two kernels:
 //  * tiled:  a workgroup computes a BN x BM tile of out^T.  Per 128-wide k step
 //    it stages BN rows of compressed weight (64 B values + 16 B metadata per
-//    row) and BM rows of activation (128 B per row) in LDS, double-buffered:
-//    the global loads of step k+1 are in flight while the MFMAs of step k run.
-//    LDS rows are XOR-swizzled in 16-byte chunks so that the 16 lanes of a
-//    quarter-wave read 16 different 16-byte bank groups.  Tiles are assigned so
-//    that each XCD (workgroup id mod 8) works on one contiguous run of tiles,
-//    walked in groups of G n-tiles, which keeps the weight and activation
-//    panels that neighbouring workgroups share in that XCD's L2.
+//    row) and BM rows of activation (128 B per row) in LDS with
+//    global_load_lds (memory -> LDS without passing through registers), in S
+//    buffers: the loads of step k+S-1 are in flight while the MFMAs of step k
+//    run.  LDS rows are XOR-swizzled in 16-byte chunks so that the 8 lanes the
+//    LDS serves together read 8 different 16-byte bank groups.  Tiles are
+//    assigned so that each XCD (workgroup id mod 8) works on one contiguous
+//    run of tiles, walked in groups of G n-tiles, which keeps the weight and
+//    activation panels that neighbouring workgroups share in that XCD's L2.
+//    The prefill shape runs 256 x 256 tiles on 8 wavefronts (64 x 128 each,
+//    two per SIMD) with S = 2; each wavefront reads its activation blocks
+//    first and then streams its weight blocks one ahead of their MFMAs.
 //  * decode: for M <= 16, where the weight read is everything.  A workgroup
-//    owns 16 weight rows; its eight wavefronts split the k steps between them,
+//    owns 16 weight rows; its wavefronts split the k steps between them,
 //    stream the compressed weight straight from HBM into registers (no LDS
 //    staging: every byte is used by exactly one instruction), and reduce
 //    their partial 16x16 sums through LDS in a fixed order (deterministic).
@@ -75,29 +79,111 @@ __device__ __forceinline__ v4f epilogue4(v4f acc, float xsm, const float* __rest
 // ---------------------------------------------------------------------------
 // Tiled kernel
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G>
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// wait for every outstanding global->LDS load, including later stages').  Each
+// wavefront waits for its own loads of the stage it is about to read before
+// arriving; the empty asm keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS row swizzles (16-byte chunks).  The LDS serves a 128-bit read 8 lanes at
+// a time, 128 bytes per clock; the 8 lanes of a group read 8 consecutive rows
+// at the same logical chunk, so the physical chunk is XORed with the row such
+// that those 8 reads cover all 32 banks exactly once.
+//   activation rows (128 B = 8 chunks): chunk ^ (row & 7)
+//   weight rows     (64 B = 4 chunks, two rows per 128 B): chunk ^ ((row >> 1) & 3)
+__device__ __forceinline__ int x_chunk(int row, int j) { return j ^ (row & 7); }
+__device__ __forceinline__ int w_chunk(int row, int j) { return j ^ ((row >> 1) & 3); }
+
+template <int BN, int BM, int WN, int WM, int S>
 struct Tiled {
-  static constexpr int NT = 64 * WN * WM;
+  static constexpr int NW = WN * WM, NT = 64 * NW;
   static constexpr int TN = BN / WN, TM = BM / WM;  // wavefront tile
   static constexpr int FN = TN / 16, FM = TM / 16;  // 16x16 blocks per wavefront
   static constexpr int W_BYTES = BN * 64, META_BYTES = BN * 16, X_BYTES = BM * 128;
   static constexpr int STAGE = W_BYTES + META_BYTES + X_BYTES;
-  static constexpr int LDS = 2 * STAGE;
-  // 16-byte chunks per stage and per thread
-  static constexpr int W_CH = BN * 4, M_CH = BN, X_CH = BM * 8;
-  static constexpr int W_PT = (W_CH + NT - 1) / NT, M_PT = (M_CH + NT - 1) / NT, X_PT = (X_CH + NT - 1) / NT;
-  static_assert(BN % (16 * WN) == 0 && BM % (16 * WM) == 0, "tile");
-  static_assert(W_CH % NT == 0 || W_PT == 1, "weight chunks");
-  static_assert(X_CH % NT == 0, "activation chunks");
+  static constexpr int LDS = S * STAGE;
+  static_assert(BN % 64 == 0 && BM % 8 == 0, "tile");
+  static_assert(BN % (16 * WN) == 0 && BM % (16 * WM) == 0, "wave tile");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(S >= 2, "stages");
 };
 
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G>
+// Global -> LDS loader of one pipeline stage.  The stage is W_INSTR + M_INSTR
+// + X_INSTR load instructions of 1 KB (64 lanes x 16 bytes, written to LDS at
+// 1024 q + 16 lane); each region is split evenly over the wavefronts.  The XOR
+// swizzle of the LDS rows is applied by choosing which global chunk a lane
+// fetches; a lane's chunk is the same for every instruction of a region (the
+// swizzles depend on row bits that one instruction's 16 or 8 rows do not
+// change), so only the row moves.  Rows past the matrix edge are clamped to
+// the last row (read, never stored).
+template <int BN, int BM, int NW>
+struct StageLoader {
+  static constexpr int W_INSTR = BN / 16, M_INSTR = BN / 64, X_INSTR = BM / 8;
+  static constexpr int W_PW = W_INSTR / NW, X_PW = X_INSTR / NW;
+  static constexpr int M_PW = (M_INSTR + NW - 1) / NW;
+  static constexpr int PER_WAVE_MIN = W_PW + X_PW + M_INSTR / NW;  // loads per stage, every wavefront
+  static_assert(W_INSTR % NW == 0 && X_INSTR % NW == 0, "loads split evenly");
+  static_assert(M_INSTR % NW == 0 || M_INSTR < NW, "metadata loads");
+  const uint8_t* values;
+  const uint8_t* meta;
+  const uint8_t* xq;
+  int64_t ldv, ldm, ldx;
+  int n_last, m_last;
+  int w_row0, w_col, m_row0, x_row0, x_col;
+  int wave;
+
+  __device__ StageLoader(const uint8_t* v, const uint8_t* mt, const uint8_t* x, int K, int N, int M, int n0, int m0,
+                         int wave_, int lane)
+      : values(v), meta(mt), xq(x), ldv(K / 2), ldm(K / 8), ldx(K), n_last(N - 1), m_last(M - 1), wave(wave_) {
+    w_row0 = n0 + wave * W_PW * 16 + (lane >> 2);
+    w_col = 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+    m_row0 = n0 + wave * 64 + lane;
+    x_row0 = m0 + wave * X_PW * 8 + (lane >> 3);
+    x_col = 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  }
+
+  __device__ __forceinline__ void issue(uint8_t* stage_base, int kt) const {
+    const int64_t kb = (int64_t)kt * 128;
+#pragma unroll
+    for (int j = 0; j < W_PW; ++j) {
+      const uint8_t* g = values + (int64_t)min(w_row0 + 16 * j, n_last) * ldv + w_col + kb / 2;
+      __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (wave * W_PW + j) * 1024), 16, 0, 0);
+    }
+    if (M_INSTR >= NW || wave < M_INSTR) {
+#pragma unroll
+      for (int j = 0; j < M_PW; ++j) {
+        const uint8_t* g = meta + (int64_t)min(m_row0 + 64 * NW * j, n_last) * ldm + kb / 8;
+        __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (W_INSTR + wave + NW * j) * 1024), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < X_PW; ++j) {
+      const uint8_t* g = xq + (int64_t)min(x_row0 + 8 * j, m_last) * ldx + x_col + kb;
+      __builtin_amdgcn_global_load_lds((void*)g,
+                                       (void*)(stage_base + (W_INSTR + M_INSTR + wave * X_PW + j) * 1024), 16, 0, 0);
+    }
+  }
+};
+
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD>
 __global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
-  using C = Tiled<XF, WF, OUT, BN, BM, WN, WM, G>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using C = Tiled<BN, BM, WN, WM, S>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // ---- tile assignment: contiguous runs per XCD, grouped along n ----
   const int T = tiles_m * tiles_n;
@@ -116,82 +202,26 @@ __global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave / WM, wm = wave % WM;
   const int r16 = lane & 15, lg = lane >> 4;
-
   const int64_t ldv = K / 2, ldm = K / 8, ldx = K;
 
-  // ---- global -> register staging addresses (rows clamped into range) ----
-  const uint8_t* gw[C::W_PT];
-  int sw_off[C::W_PT];
-  bool w_on[C::W_PT];
-#pragma unroll
-  for (int i = 0; i < C::W_PT; ++i) {
-    const int c = tid + i * C::NT;
-    w_on[i] = c < C::W_CH;
-    const int r = (c >> 2) % BN, j = c & 3;
-    const int64_t row = min(n0 + r, N - 1);
-    gw[i] = values + row * ldv + 16 * j;
-    sw_off[i] = r * 64 + 16 * (j ^ ((r >> 2) & 3));
-  }
-  const uint8_t* gm[C::M_PT];
-  int sm_off[C::M_PT];
-  bool m_on[C::M_PT];
-#pragma unroll
-  for (int i = 0; i < C::M_PT; ++i) {
-    const int r = tid + i * C::NT;
-    m_on[i] = r < C::M_CH;
-    const int64_t row = min(n0 + (r % BN), N - 1);
-    gm[i] = meta + row * ldm;
-    sm_off[i] = C::W_BYTES + (r % BN) * 16;
-  }
-  const uint8_t* gx[C::X_PT];
-  int sx_off[C::X_PT];
-#pragma unroll
-  for (int i = 0; i < C::X_PT; ++i) {
-    const int c = tid + i * C::NT;
-    const int r = c >> 3, j = c & 7;
-    const int64_t row = min(m0 + r, M - 1);
-    gx[i] = xq + row * ldx + 16 * j;
-    sx_off[i] = C::W_BYTES + C::META_BYTES + r * 128 + 16 * (j ^ ((r >> 1) & 7));
-  }
-
-  uint4 rw[C::W_PT], rm[C::M_PT], rx[C::X_PT];
-  auto gload = [&](int kt) {
-    const int64_t kb = (int64_t)kt * KSTEP;
-#pragma unroll
-    for (int i = 0; i < C::W_PT; ++i)
-      if (w_on[i]) rw[i] = *reinterpret_cast<const uint4*>(gw[i] + kb / 2);
-#pragma unroll
-    for (int i = 0; i < C::M_PT; ++i)
-      if (m_on[i]) rm[i] = *reinterpret_cast<const uint4*>(gm[i] + kb / 8);
-#pragma unroll
-    for (int i = 0; i < C::X_PT; ++i) rx[i] = *reinterpret_cast<const uint4*>(gx[i] + kb);
-  };
-  auto sstore = [&](int stage) {
-    uint8_t* base = smem + stage * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::W_PT; ++i)
-      if (w_on[i]) *reinterpret_cast<uint4*>(base + sw_off[i]) = rw[i];
-#pragma unroll
-    for (int i = 0; i < C::M_PT; ++i)
-      if (m_on[i]) *reinterpret_cast<uint4*>(base + sm_off[i]) = rm[i];
-#pragma unroll
-    for (int i = 0; i < C::X_PT; ++i) *reinterpret_cast<uint4*>(base + sx_off[i]) = rx[i];
-  };
+  // ---- this wavefront's share of the per-stage loads (global -> LDS) ----
+  const StageLoader<BN, BM, C::NW> loader(values, meta, xq, K, N, M, n0, m0, wave, lane);
+  auto issue = [&](int kt, int slot) { loader.issue(smem + slot * C::STAGE, kt); };
+  constexpr int LPW = StageLoader<BN, BM, C::NW>::PER_WAVE_MIN;
 
   // ---- LDS read offsets of this lane's MFMA operands ----
   int a_off[C::FN], i_off[C::FN], b_off0[C::FM], b_off1[C::FM];
 #pragma unroll
   for (int f = 0; f < C::FN; ++f) {
     const int r = wn * C::TN + f * 16 + r16;
-    a_off[f] = r * 64 + 16 * (lg ^ ((r >> 2) & 3));
+    a_off[f] = r * 64 + 16 * w_chunk(r, lg);
     i_off[f] = C::W_BYTES + r * 16 + 4 * lg;
   }
 #pragma unroll
   for (int f = 0; f < C::FM; ++f) {
     const int r = wm * C::TM + f * 16 + r16;
-    const int sw = (r >> 1) & 7;
-    b_off0[f] = C::W_BYTES + C::META_BYTES + r * 128 + 16 * (lg ^ sw);
-    b_off1[f] = C::W_BYTES + C::META_BYTES + r * 128 + 16 * ((4 + lg) ^ sw);
+    b_off0[f] = C::W_BYTES + C::META_BYTES + r * 128 + 16 * x_chunk(r, lg);
+    b_off1[f] = C::W_BYTES + C::META_BYTES + r * 128 + 16 * x_chunk(r, 4 + lg);
   }
 
   v4f acc[C::FN][C::FM];
@@ -201,29 +231,61 @@ __global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
     for (int j = 0; j < C::FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int KT = K / KSTEP;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue(s, s);
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t* base = smem + cur * C::STAGE;
-    v8i b[C::FM];
+    // stage kt has landed once at most the loads of the S-2 later stages are pending
+    if (kt + S - 2 < KT) wait_vmcnt<LPW * (S - 2)>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const uint8_t* base = smem + (kt % S) * C::STAGE;
+    if constexpr (ORD == 0) {
+      // all weight operands of the wavefront tile, then one activation block at
+      // a time: each 32-byte B fragment feeds FN instructions
+      v4i a[C::FN];
+      int idx[C::FN];
 #pragma unroll
-    for (int f = 0; f < C::FM; ++f) {
-      const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[f]);
-      const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[f]);
-      b[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int fn = 0; fn < C::FN; ++fn) {
+        a[fn] = *reinterpret_cast<const v4i*>(base + a_off[fn]);
+        idx[fn] = *reinterpret_cast<const int*>(base + i_off[fn]);
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+        const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16<XF, WF>(a[fn], b, acc[fn][fm], idx[fn]);
+      }
+    } else {
+      // all activation blocks, then the weight blocks one ahead of their MFMAs
+      v8i b[C::FM];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+        b[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      v4i a[2];
+      int idx[2];
+      a[0] = *reinterpret_cast<const v4i*>(base + a_off[0]);
+      idx[0] = *reinterpret_cast<const int*>(base + i_off[0]);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        if (fn + 1 < C::FN) {
+          a[(fn + 1) & 1] = *reinterpret_cast<const v4i*>(base + a_off[fn + 1]);
+          idx[(fn + 1) & 1] = *reinterpret_cast<const int*>(base + i_off[fn + 1]);
+        }
+        if constexpr (ORD == 2) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+          acc[fn][fm] = smfmac16<XF, WF>(a[fn & 1], b[fm], acc[fn][fm], idx[fn & 1]);
+        if constexpr (ORD == 2) __builtin_amdgcn_s_setprio(0);
+      }
     }
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const v4i a = *reinterpret_cast<const v4i*>(base + a_off[fn]);
-      const int idx = *reinterpret_cast<const int*>(base + i_off[fn]);
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) acc[fn][fm] = smfmac16<XF, WF>(a, b[fm], acc[fn][fm], idx);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: scales, bias, bf16, store ----
@@ -244,15 +306,16 @@ __global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16)
 // ---------------------------------------------------------------------------
-constexpr int DEC_WAVES = 8;
-constexpr int DEC_UNROLL = 4;
-
-template <int XF, int WF, int OUT>
-__global__ __launch_bounds__(64 * DEC_WAVES) void linear_decode_kernel(
+// NWV wavefronts per workgroup, each taking k steps wave, wave + NWV, ... (U of
+// them per pass).  All of a pass's loads are issued before its first MFMA and
+// nothing in between branches, so a wavefront has U * 4 loads in flight.
+// Steps past the end re-read the last step (in bounds) and add a zero A operand.
+template <int XF, int WF, int OUT, int NWV, int U>
+__global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K) {
-  __shared__ v4f red[DEC_WAVES][64];
+  __shared__ v4f red[NWV][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, lg = lane >> 4;
@@ -263,53 +326,74 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void linear_decode_kernel(
   const uint8_t* mrow = meta + (int64_t)(n0 + r16) * (K / 8) + 4 * lg;
   const bool xon = r16 < M;
   const uint8_t* xrow = xq + (int64_t)min(r16, M - 1) * K + 16 * lg;
+  const v4i z4 = v4i{0, 0, 0, 0};
+
+  // epilogue operands, fetched up front so their latency hides under the stream
+  const int m = r16, n = n0 + 4 * lg;
+  float xsm = 0.f;
+  v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
+  uint2 b2 = make_uint2(0, 0);
+  if (wave == 0) {
+    xsm = xs[min(m, M - 1)];
+    w4 = *reinterpret_cast<const v4f*>(ws + n);
+    if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
+  }
 
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < KT; s0 += DEC_WAVES * DEC_UNROLL) {
-    v4i a[DEC_UNROLL];
-    int idx[DEC_UNROLL];
-    v8i b[DEC_UNROLL];
+  for (int s0 = wave; s0 < KT; s0 += NWV * U) {
+    v4i a[U], blo[U], bhi[U];
+    int idx[U];
 #pragma unroll
-    for (int u = 0; u < DEC_UNROLL; ++u) {
-      const int s = s0 + u * DEC_WAVES;
-      if (s < KT) {
-        a[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vrow + (int64_t)s * 64));
-        idx[u] = __builtin_nontemporal_load(reinterpret_cast<const int*>(mrow + (int64_t)s * 16));
-        if (xon) {
-          const v4i lo = *reinterpret_cast<const v4i*>(xrow + (int64_t)s * 128);
-          const v4i hi = *reinterpret_cast<const v4i*>(xrow + (int64_t)s * 128 + 64);
-          b[u] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          b[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = min(s0 + u * NWV, KT - 1);
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vrow + s * 64));
+      idx[u] = __builtin_nontemporal_load(reinterpret_cast<const int*>(mrow + s * 16));
     }
 #pragma unroll
-    for (int u = 0; u < DEC_UNROLL; ++u)
-      if (s0 + u * DEC_WAVES < KT) acc = smfmac16<XF, WF>(a[u], b[u], acc, idx[u]);
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = min(s0 + u * NWV, KT - 1);
+      blo[u] = *reinterpret_cast<const v4i*>(xrow + s * 128);
+      bhi[u] = *reinterpret_cast<const v4i*>(xrow + s * 128 + 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the pass ahead of the MFMAs
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = s0 + u * NWV < KT;
+      const v4i av = live ? a[u] : z4;
+      const v4i lo = xon ? blo[u] : z4, hi = xon ? bhi[u] : z4;
+      const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = smfmac16<XF, WF>(av, b, acc, idx[u]);
+    }
   }
   red[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
     v4f t = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < DEC_WAVES; ++w) t += red[w][lane];
-    const int m = r16;
-    const int n = n0 + 4 * lg;
-    if (m < M) store4<OUT>(out, N, m, n, epilogue4(t, xs[m], ws, bias, n));
+    for (int w = 1; w < NWV; ++w) t += red[w][lane];
+    v4f y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
+    if (bias) {
+      y[0] += bf16_to_f32(b2.x & 0xFFFFu);
+      y[1] += bf16_to_f32(b2.x >> 16);
+      y[2] += bf16_to_f32(b2.y & 0xFFFFu);
+      y[3] += bf16_to_f32(b2.y >> 16);
+    }
+    if (m < M) store4<OUT>(out, N, m, n, y);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0>
 hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
-  using C = Tiled<XF, WF, OUT, BN, BM, WN, WM, G>;
+  using C = Tiled<BN, BM, WN, WM, S>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G>;
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -325,15 +409,25 @@ hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
 template <int XF, int WF, int OUT>
 hipError_t run_linear(const LinearArgs& a, hipStream_t stream) {
   if (a.m <= 16) {
-    hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT>), dim3((unsigned)(a.n / 16)), dim3(64 * DEC_WAVES), 0,
-                       stream, a.xq, a.xs, a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k);
+    const int64_t kt = a.k / KSTEP;
+    const dim3 grid((unsigned)(a.n / 16));
+#define SFR_DEC(NWV, U)                                                                                      \
+  hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT, NWV, U>), grid, dim3(64 * NWV), 0, stream, a.xq, a.xs, \
+                     a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k)
+    if (kt <= 8) SFR_DEC(8, 1);
+    else if (kt <= 16) SFR_DEC(8, 2);
+    else if (kt <= 32) SFR_DEC(8, 4);
+    else if (kt <= 64) SFR_DEC(16, 4);
+    else if (kt <= 112) SFR_DEC(16, 7);
+    else SFR_DEC(16, 8);  // loops for kt > 128
+#undef SFR_DEC
     return hipGetLastError();
   }
   const int64_t big = ((a.m + 255) / 256) * ((a.n + 255) / 256);
   const int64_t mid = ((a.m + 127) / 128) * ((a.n + 127) / 128);
-  if (big >= 512) return run_tiled<XF, WF, OUT, 256, 256, 2, 4, 8>(a, stream);
-  if (mid >= 256) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8>(a, stream);
-  return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8>(a, stream);
+  if (big >= 512) return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
+  if (mid >= 256) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
+  return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
 }
 
 template <int XF, int WF>
