@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
 // them per pass).  All of a pass's loads are issued before its first MFMA and
 // nothing in between branches, so a wavefront has U * 4 loads in flight.
 // Steps past the end re-read the last step (in bounds) and add a zero A operand.
-template <int XF, int WF, int OUT, int NWV, int U>
+template <int XF, int WF, int OUT, int NWV, int U, bool NT = true>
 __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -346,8 +346,13 @@ __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = min(s0 + u * NWV, KT - 1);
-      a[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vrow + s * 64));
-      idx[u] = __builtin_nontemporal_load(reinterpret_cast<const int*>(mrow + s * 16));
+      if constexpr (NT) {
+        a[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vrow + s * 64));
+        idx[u] = __builtin_nontemporal_load(reinterpret_cast<const int*>(mrow + s * 16));
+      } else {
+        a[u] = *reinterpret_cast<const v4i*>(vrow + s * 64);
+        idx[u] = *reinterpret_cast<const int*>(mrow + s * 16);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -371,6 +376,150 @@ __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
     v4f t = red[0][lane];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) t += red[w][lane];
+    v4f y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
+    if (bias) {
+      y[0] += bf16_to_f32(b2.x & 0xFFFFu);
+      y[1] += bf16_to_f32(b2.x >> 16);
+      y[2] += bf16_to_f32(b2.y & 0xFFFFu);
+      y[3] += bf16_to_f32(b2.y >> 16);
+    }
+    if (m < M) store4<OUT>(out, N, m, n, y);
+  }
+}
+
+// Decode kernel, LDS-staged variant.  A workgroup of 4 wavefronts owns 16
+// weight rows.  Their compressed values (16 x K/2 bytes) and metadata
+// (16 x K/8 bytes) are one contiguous block each in memory, so they are read
+// with 1 KB contiguous global_load_lds instructions into LDS, then each
+// wavefront runs the MFMAs of a quarter of the k steps from there.  Chunks are
+// XOR-swizzled within their 128-byte group by (row & 7) on the way in (a
+// permutation inside each 1 KB load, so reads stay contiguous), which makes the
+// MFMA-layout reads conflict-free.  The activation is read directly.
+template <int XF, int WF, int OUT, bool XL>
+__global__ __launch_bounds__(256) void linear_decode_lds_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
+    const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
+    void* __restrict__ out, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int KT = K / KSTEP;
+  const int vbytes = 16 * (K / 2), mbytes = 16 * (K / 8);  // multiples of 1 KB (K % 128 == 0)
+  const uint8_t* vblk = values + (int64_t)n0 * (K / 2);
+  const uint8_t* mblk = meta + (int64_t)n0 * (K / 8);
+  const int vchunks_row = K / 32, mchunks_row = K / 128;   // 16-byte chunks per row
+
+  // epilogue operands up front
+  const int m = r16, n = n0 + 4 * lg;
+  float xsm = 0.f;
+  v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
+  uint2 b2 = make_uint2(0, 0);
+  if (wave == 0) {
+    xsm = xs[min(m, M - 1)];
+    w4 = *reinterpret_cast<const v4f*>(ws + n);
+    if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
+  }
+  // stream the block into LDS: LDS chunk p holds global chunk p ^ (row(p) & 7)
+  for (int q = wave; q < vbytes / 1024; q += 4) {
+    const int p = q * 64 + lane, row = p / vchunks_row;
+    __builtin_amdgcn_global_load_lds((void*)(vblk + 16 * (p ^ (row & 7))), (void*)(smem + q * 1024), 16, 0, 0);
+  }
+  for (int q = wave; q < mbytes / 1024; q += 4) {
+    const int p = q * 64 + lane, row = p / mchunks_row;
+    __builtin_amdgcn_global_load_lds((void*)(mblk + 16 * (p ^ (row & 7))), (void*)(smem + vbytes + q * 1024), 16, 0,
+                                     0);
+  }
+  const int s_lo = (KT * wave) / 4, s_hi = (KT * (wave + 1)) / 4;
+  const bool xon = r16 < M;
+  const v4i z4 = v4i{0, 0, 0, 0};
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  if constexpr (XL) {
+    // the M activation rows (M * K contiguous bytes) follow the weight block in
+    // LDS, swizzled the same way; rows >= M are never read (clamped, zeroed)
+    const int xchunks_row = K / 16, xoff = vbytes + mbytes;
+    for (int q = wave; q < (M * K) / 1024; q += 4) {
+      const int p = q * 64 + lane, row = p / xchunks_row;
+      __builtin_amdgcn_global_load_lds((void*)(xq + 16 * (p ^ (row & 7))), (void*)(smem + xoff + q * 1024), 16, 0,
+                                       0);
+    }
+    wait_vmcnt<0>();
+    stage_barrier();
+    const int xr = min(r16, M - 1);
+    // groups of 4 steps: all LDS reads of a group first, then its MFMAs into
+    // two accumulators (so consecutive MFMAs do not wait on each other)
+    v4f acc2 = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = s_lo; s0 < s_hi; s0 += 4) {
+      v4i a[4], lo[4], hi[4];
+      int idx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = min(s0 + u, s_hi - 1);
+        const int pv = r16 * vchunks_row + 4 * s + lg;
+        const int pm = r16 * mchunks_row + s;
+        const int px = xr * xchunks_row + 8 * s + lg;
+        a[u] = *reinterpret_cast<const v4i*>(smem + 16 * (pv ^ (r16 & 7)));
+        idx[u] = *reinterpret_cast<const int*>(smem + vbytes + 16 * (pm ^ (r16 & 7)) + 4 * lg);
+        lo[u] = *reinterpret_cast<const v4i*>(smem + xoff + 16 * (px ^ (xr & 7)));
+        hi[u] = *reinterpret_cast<const v4i*>(smem + xoff + 16 * ((px + 4) ^ (xr & 7)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool live = s0 + u < s_hi;
+        const v4i av = live ? a[u] : z4;
+        const v4i l = xon ? lo[u] : z4, h = xon ? hi[u] : z4;
+        const v8i b = v8i{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+        if (u & 1) acc2 = smfmac16<XF, WF>(av, b, acc2, idx[u]);
+        else acc = smfmac16<XF, WF>(av, b, acc, idx[u]);
+      }
+    }
+    acc += acc2;
+  } else {
+    // activation operands straight from memory, in chunks of SPW steps; the
+    // first chunk is in flight with the weight stream
+    constexpr int SPW = 8;
+    const uint8_t* xrow = xq + (int64_t)min(r16, M - 1) * K + 16 * lg;
+    v4i xlo[SPW], xhi[SPW];
+    auto load_x = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) {
+        const int64_t s = min(c0 + u, KT - 1);
+        xlo[u] = *reinterpret_cast<const v4i*>(xrow + s * 128);
+        xhi[u] = *reinterpret_cast<const v4i*>(xrow + s * 128 + 64);
+      }
+    };
+    load_x(s_lo);
+    wait_vmcnt<0>();
+    stage_barrier();
+    for (int c0 = s_lo; c0 < s_hi; c0 += SPW) {
+      if (c0 != s_lo) load_x(c0);
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) {
+        const int s = c0 + u;
+        if (s < s_hi) {
+          const int pv = r16 * vchunks_row + 4 * s + lg;  // chunk of row r16, step s, lane group lg
+          const int pm = r16 * mchunks_row + s;            // metadata chunk of row r16, step s
+          const v4i a = *reinterpret_cast<const v4i*>(smem + 16 * (pv ^ (r16 & 7)));
+          const int idx = *reinterpret_cast<const int*>(smem + vbytes + 16 * (pm ^ (r16 & 7)) + 4 * lg);
+          const v4i lo = xon ? xlo[u] : z4, hi = xon ? xhi[u] : z4;
+          const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc = smfmac16<XF, WF>(a, b, acc, idx);
+        }
+      }
+    }
+  }
+  // fixed-order reduction of the 4 partial tiles (LDS reused after a barrier)
+  stage_barrier();
+  v4f* red = reinterpret_cast<v4f*>(smem);
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f t = red[lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) t += red[w * 64 + lane];
     v4f y;
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
@@ -409,6 +558,24 @@ hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
 template <int XF, int WF, int OUT>
 hipError_t run_linear(const LinearArgs& a, hipStream_t stream) {
   if (a.m <= 16) {
+    // LDS-staged decode when the 16-row weight block (10 K bytes) fits in LDS,
+    // with the activation staged too when it also fits
+    constexpr int64_t kLds = 160 * 1024;
+    if (a.k % 1024 == 0 && 10 * a.k <= kLds) {
+      const bool xl = 10 * a.k + a.m * a.k <= kLds;
+      const unsigned lds = (unsigned)(10 * a.k + (xl ? a.m * a.k : 0));
+      auto kern = xl ? linear_decode_lds_kernel<XF, WF, OUT, true> : linear_decode_lds_kernel<XF, WF, OUT, false>;
+      static bool attr_set[2] = {false, false};  // benign race: every thread sets the same value
+      if (!attr_set[xl]) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        if (e != hipSuccess) return e;
+        attr_set[xl] = true;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(256), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
+                         a.bias, a.out, (int)a.m, (int)a.n, (int)a.k);
+      return hipGetLastError();
+    }
     const int64_t kt = a.k / KSTEP;
     const dim3 grid((unsigned)(a.n / 16));
 #define SFR_DEC(NWV, U)                                                                                      \

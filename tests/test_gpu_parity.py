@@ -162,12 +162,19 @@ def test_linear_decode(gpu, case):
 
 
 # ragged shapes that land on each tile configuration (64x64, 128x128, 256x256)
+# and on each decode variant
 RAGGED = [
     sfr_inputs.Case("ragged", 6, 100, 1040, 384, x_fmt=E4, w_fmt=E5, bias=True),
     sfr_inputs.Case("ragged", 6, 17, 4096, 256, x_fmt=E5, w_fmt=E4),
     sfr_inputs.Case("ragged", 6, 1000, 4112, 256, x_fmt=E4, w_fmt=E4, bias=True),
     sfr_inputs.Case("ragged", 6, 4100, 8208, 256, x_fmt=E5, w_fmt=E5),
     sfr_inputs.Case("ragged", 6, 2, 144, 128, x_fmt=E4, w_fmt=E4, bias=True),
+    # decode kernels: LDS-staged with and without the activation in LDS, and
+    # the largest K whose weight block fills the whole LDS
+    sfr_inputs.Case("ragged", 6, 3, 64, 1024, x_fmt=E5, w_fmt=E4, bias=True),
+    sfr_inputs.Case("ragged", 6, 16, 32, 16384, x_fmt=E4, w_fmt=E5),
+    sfr_inputs.Case("ragged", 6, 1, 48, 16384, x_fmt=E5, w_fmt=E5, bias=True),
+    sfr_inputs.Case("ragged", 6, 7, 96, 2048, x_fmt=E4, w_fmt=E4),
 ]
 
 
