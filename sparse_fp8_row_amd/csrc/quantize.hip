@@ -8,6 +8,11 @@
 // over the bf16 magnitude bits, reduced inside one wavefront, so no atomics
 // and no cross-workgroup step exist at all.
 //
+// The per-element division x / scale is done as a multiplication by the
+// row's reciprocal with an exactness check (cast8): the IEEE
+// division runs only for the rare elements whose FP8 rounding the check cannot
+// settle, so the codes are those of the plain division.
+//
 // Layout: one 64-lane wavefront owns one row.  Lane l holds 16-byte chunks
 // (8 bf16) l, l+64, l+128, ... of its row in registers between the amax sweep
 // and the cast sweep, so each input byte is read from HBM once.  Rows longer
@@ -38,17 +43,55 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
   return m;
 }
 
-// 8 bf16 -> 8 FP8 bytes.  `scale` > 0: x / scale (IEEE binary32 division),
-// clamped to +/-fmax, rounded to nearest even by the hardware converter.
+// True when q = fl32(x * rcp) is known to encode to the same FP8 code as
+// fl32(x / scale) (see cast8).
 template <int FMT>
-__device__ __forceinline__ uint2 cast8(uint4 c, float scale) {
+__device__ __forceinline__ bool quotient_settled(float x, float q) {
+  constexpr uint32_t kMinNormal = (FMT == FMT_E4M3) ? 0x3C800000u : 0x38800000u;  // 2^-6, 2^-14
+  constexpr uint32_t kLowMask = (FMT == FMT_E4M3) ? 0xFFFFFu : 0x1FFFFFu;
+  constexpr uint32_t kMid = (FMT == FMT_E4M3) ? 0x80000u : 0x100000u;
+  const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
+  const uint32_t low = b & kLowMask;
+  const uint32_t dist = low > kMid ? low - kMid : kMid - low;
+  return (b >= kMinNormal && b < 0x7F800000u && dist > 8u) || x == 0.0f;
+}
+
+// 8 bf16 -> 8 FP8 bytes.  `scale` > 0, `rcp` = fl32(1 / scale): the codes of
+// fl32(x / scale) (IEEE binary32 division), clamped to +/-fmax and rounded to
+// nearest even by the hardware converter.
+//
+// The quotients are formed as q = fl32(x * rcp), which differs from x / scale
+// by at most 2^-23 relative, so fl32(x / scale) lies within a few binary32
+// steps of q.  An FP8 code only changes where the value crosses the midpoint
+// between two FP8 neighbours; in the FP8 normal range that midpoint has the
+// low 20 (e4m3) or 21 (e5m2) bits of the binary32 pattern equal to 0x80000 /
+// 0x100000.  When q's low bits are more than 8 steps from it, q and
+// fl32(x / scale) round to the same code (at binade edges the low bits are
+// near 0 or all ones, far from the midpoint).  Zero divides to a signed zero
+// (taken as is: rcp is infinite when scale is below 2^-128).  An element the
+// test cannot settle -- near a midpoint, in the FP8 subnormal
+// range, or not finite -- takes the IEEE division (one branch per 8 elements).
+template <int FMT>
+__device__ __forceinline__ uint2 cast8(uint4 c, float scale, float rcp) {
   constexpr float fmax = Fp8<FMT>::fmax;
   uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float t[8];
+  float x[8], t[8];
+  bool settled = true;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    t[2 * i] = bf16_to_f32(w[i] & 0xFFFFu) / scale;
-    t[2 * i + 1] = bf16_to_f32(w[i] >> 16) / scale;
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // a zero keeps its sign (x * rcp would give NaN when rcp is infinite)
+    t[i] = x[i] == 0.0f ? x[i] : x[i] * rcp;
+    settled = settled && quotient_settled<FMT>(x[i], t[i]);
+  }
+  if (__builtin_expect(!settled, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!quotient_settled<FMT>(x[i], t[i])) t[i] = x[i] / scale;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(t[i], -fmax), fmax);
@@ -85,16 +128,23 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
   if constexpr (R > 0) {
     uint4 buf[R];
     uint32_t m = 0;
+    if (nchunks == 64 * R) {
+      // whole row in R chunks per lane: unconditional loads, all in flight at once
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int64_t c = lane + 64 * i;
-      buf[i] = c < nchunks ? xr[c] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < R; ++i) buf[i] = xr[lane + 64 * i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t c = lane + 64 * i;
+        buf[i] = c < nchunks ? xr[c] : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) m = mag_max8(buf[i], m);
     m = wave_max(m);
     const float amax = bf16_to_f32(m);
     const float s = amax / Fp8<FMT>::fmax;
+    const float r = 1.0f / s;
     if (lane == 0) scale[row] = (m == 0) ? 0.0f : s;
     if (m == 0) {
 #pragma unroll
@@ -106,7 +156,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int64_t c = lane + 64 * i;
-        if (c < nchunks) qr[c] = cast8<FMT>(buf[i], s);
+        if (c < nchunks) qr[c] = cast8<FMT>(buf[i], s, r);
       }
     }
   } else {
@@ -115,11 +165,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
     m = wave_max(m);
     const float amax = bf16_to_f32(m);
     const float s = amax / Fp8<FMT>::fmax;
+    const float r = 1.0f / s;
     if (lane == 0) scale[row] = (m == 0) ? 0.0f : s;
     if (m == 0) {
       for (int64_t c = lane; c < nchunks; c += 64) qr[c] = zero8(xr[c]);
     } else {
-      for (int64_t c = lane; c < nchunks; c += 64) qr[c] = cast8<FMT>(xr[c], s);
+      for (int64_t c = lane; c < nchunks; c += 64) qr[c] = cast8<FMT>(xr[c], s, r);
     }
   }
 }
@@ -130,11 +181,14 @@ hipError_t launch_fmt(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
   const int64_t per_lane = ((cols >> 3) + 63) / 64;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
 #define SFR_Q(R) hipLaunchKernelGGL((quantize_rows_kernel<FMT, R>), grid, block, 0, stream, x, rows, cols, q, scale)
+  // R = chunks per lane; rows of exactly 64 * R chunks (K = 4096 -> 8, K = 14336
+  // -> 28) take the unconditional-load path
   if (per_lane <= 1) SFR_Q(1);
   else if (per_lane <= 2) SFR_Q(2);
   else if (per_lane <= 4) SFR_Q(4);
   else if (per_lane <= 8) SFR_Q(8);
   else if (per_lane <= 16) SFR_Q(16);
+  else if (per_lane <= 28) SFR_Q(28);
   else if (per_lane <= 32) SFR_Q(32);
   else SFR_Q(0);
 #undef SFR_Q
