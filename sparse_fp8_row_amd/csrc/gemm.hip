@@ -177,8 +177,8 @@ struct StageLoader {
   }
 };
 
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD>
-__global__ __launch_bounds__(64 * WN * WM) void linear_tiled_kernel(
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC>
+__global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
@@ -536,13 +536,13 @@ __global__ __launch_bounds__(256) void linear_decode_lds_kernel(
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1>
 hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, S>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD>;
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
