@@ -212,7 +212,7 @@ def main():
                                "e4m3 x e4m3, bf16 out, no bias",
                    "m": M, "n": N, "k": K, "x_dtype": "e4m3", "w_dtype": "e4m3", "out_dtype": "bf16",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "linear_tiled_kernel (256x256 tile)",
+        "roofline": {"bound": "mfma", "kernel": "linear_wide_kernel (256x256 tile, 4 wavefronts)",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "frac_of_sparse_peak": round(gemm_tflops / PEAK_FP8_SPARSE_TFLOPS, 4),

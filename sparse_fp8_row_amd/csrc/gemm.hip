@@ -38,6 +38,8 @@
 //    their partial 16x16 sums through LDS in a fixed order (deterministic).
 //    Tokens beyond M are zero columns of B, the padding-to-16 idea of
 //    pytorch/ao PR #1734 ("promote blocksparse from prototype ...").
+#include <type_traits>
+
 #include "sfr_device.hpp"
 #include "sfr_launch.hpp"
 
@@ -59,21 +61,47 @@ __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t
   }
 }
 
-// y = acc * (xs * ws) (+ bias), binary32.
-__device__ __forceinline__ v4f epilogue4(v4f acc, float xsm, const float* __restrict__ ws,
-                                         const uint16_t* __restrict__ bias, int64_t n) {
-  const v4f w4 = *reinterpret_cast<const v4f*>(ws + n);
-  v4f y;
+// Epilogue of a wavefront's FN x FM grid of 16x16 blocks (block (fn, fm) at
+// rows nb + 16 fn, columns mb + 16 fm of the product; lane (r16, lg) holds
+// n = 4 lg .. 4 lg + 3 of column m = r16).  Every scale and bias load is
+// issued before the first store: a wait for a load also waits for all stores
+// issued before it, so loads interleaved with the stores would each cost a
+// full store round trip.  Loads are clamped into range and the stores masked.
+template <int OUT, int FN, int FM>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float* __restrict__ xs,
+                                           const float* __restrict__ ws, const uint16_t* __restrict__ bias,
+                                           void* __restrict__ out, int M, int N, int mb, int nb, int r16, int lg) {
+  float xsv[FM];
+  v4f wsv[FN];
+  uint2 bv[FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = acc[i] * (xsm * w4[i]);
-  if (bias) {
-    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-    y[0] += bf16_to_f32(b.x & 0xFFFFu);
-    y[1] += bf16_to_f32(b.x >> 16);
-    y[2] += bf16_to_f32(b.y & 0xFFFFu);
-    y[3] += bf16_to_f32(b.y >> 16);
+  for (int fm = 0; fm < FM; ++fm) xsv[fm] = xs[min(mb + fm * 16 + r16, M - 1)];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int nc = min(nb + fn * 16 + 4 * lg, N - 4);
+    wsv[fn] = *reinterpret_cast<const v4f*>(ws + nc);
+    bv[fn] = bias ? *reinterpret_cast<const uint2*>(bias + nc) : make_uint2(0u, 0u);
   }
-  return y;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = mb + fm * 16 + r16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = nb + fn * 16 + 4 * lg;
+      if (n >= N) continue;
+      v4f y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = acc[fn][fm][i] * (xsv[fm] * wsv[fn][i]);
+      if (bias) {
+        y[0] += bf16_to_f32(bv[fn].x & 0xFFFFu);
+        y[1] += bf16_to_f32(bv[fn].x >> 16);
+        y[2] += bf16_to_f32(bv[fn].y & 0xFFFFu);
+        y[3] += bf16_to_f32(bv[fn].y >> 16);
+      }
+      store4<OUT>(out, N, m, n, y);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -152,6 +180,27 @@ struct StageLoader {
     m_row0 = n0 + wave * 64 + lane;
     x_row0 = m0 + wave * X_PW * 8 + (lane >> 3);
     x_col = 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  }
+
+  // Load j (0 <= j < PER_WAVE_MIN, a compile-time constant once unrolled) of
+  // this wavefront's share of stage kt: weight rows, then metadata, then
+  // activation rows.  Only for loaders where every wavefront has a metadata load.
+  __device__ __forceinline__ void issue_one(uint8_t* stage_base, int kt, int j) const {
+    static_assert(M_INSTR % NW == 0, "one metadata share per wavefront");
+    const int64_t kb = (int64_t)kt * 128;
+    if (j < W_PW) {
+      const uint8_t* g = values + (int64_t)min(w_row0 + 16 * j, n_last) * ldv + w_col + kb / 2;
+      __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (wave * W_PW + j) * 1024), 16, 0, 0);
+    } else if (j < W_PW + M_PW) {
+      const int q = j - W_PW;
+      const uint8_t* g = meta + (int64_t)min(m_row0 + 64 * NW * q, n_last) * ldm + kb / 8;
+      __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (W_INSTR + wave + NW * q) * 1024), 16, 0, 0);
+    } else {
+      const int q = j - W_PW - M_PW;
+      const uint8_t* g = xq + (int64_t)min(x_row0 + 8 * q, m_last) * ldx + x_col + kb;
+      __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (W_INSTR + M_INSTR + wave * X_PW + q) * 1024),
+                                       16, 0, 0);
+    }
   }
 
   __device__ __forceinline__ void issue(uint8_t* stage_base, int kt) const {
@@ -289,18 +338,218 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   }
 
   // ---- epilogue: scales, bias, bf16, store ----
+  store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg);
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined tiled kernel: 256 x 256 tile, four wavefronts (one per
+// SIMD), each owning a 128 x 128 block of the tile (64 accumulators of 16x16,
+// held in the accumulation registers).
+// ---------------------------------------------------------------------------
+// With one wavefront per SIMD nothing else hides a wavefront's own LDS latency,
+// so the reads are pipelined in registers:
+//   * the activation fragments of a k step stream through a ring of RING
+//     registers sets, read PF m blocks ahead of their MFMAs;
+//   * the weight fragments and the first PF activation fragments of step kt+1
+//     are read during the last m blocks of step kt.
+// That needs stage kt+1 in LDS before step kt ends, so the workgroup barrier
+// sits inside the step, before m block SWITCH: by then each wavefront has
+// issued every LDS read of stage kt (and waited for them), and stage kt+1 has
+// landed.  Past the barrier, stage kt's slot is free and receives stage kt+3:
+// three LDS stages give each global->LDS load two steps to land.
+template <int XF, int WF, int OUT, int G>
+__global__ __launch_bounds__(256, 1) void linear_wide_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
+    const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
+    void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int BN = 256, BM = 256, S = 3;
+  using C = Tiled<BN, BM, 2, 2, S>;
+  using L = StageLoader<BN, BM, C::NW>;
+  constexpr int FN = C::FN, FM = C::FM;  // 8 x 8
+  constexpr int LPW = L::PER_WAVE_MIN;   // global->LDS loads per stage and wavefront
+  constexpr int PF = 2, RING = 4, SWITCH = FM - PF;
+  static_assert(RING >= PF + 1 && FM % RING == 0, "activation ring");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int T = tiles_m * tiles_n;
+  const int per_xcd = (T + 7) / 8;
+  const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lid >= T) return;
+  const int group = lid / (G * tiles_m);
+  const int first_n = group * G;
+  const int gsize = min(tiles_n - first_n, G);
+  const int within = lid - group * G * tiles_m;
+  const int tn = first_n + within % gsize;
+  const int tm = within / gsize;
+  const int n0 = tn * BN, m0 = tm * BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / 2, wm = wave % 2;
+  const int r16 = lane & 15, lg = lane >> 4;
+
+  const L loader(values, meta, xq, K, N, M, n0, m0, wave, lane);
+  const int KT = K / KSTEP;
+
+  // LDS operand offsets: block f of the wavefront sits 16 f rows further on,
+  // and the swizzles depend only on row bits 0-2, which f does not change, so
+  // each offset is a per-lane base plus a compile-time multiple of f.
+  const int a_base = (wn * C::TN + r16) * 64 + 16 * w_chunk(r16, lg);        // + 1024 f
+  const int i_base = C::W_BYTES + (wn * C::TN + r16) * 16 + 4 * lg;         // + 256 f
+  const int b_base0 = C::W_BYTES + C::META_BYTES + (wm * C::TM + r16) * 128 + 16 * x_chunk(r16, lg);      // + 2048 f
+  const int b_base1 = C::W_BYTES + C::META_BYTES + (wm * C::TM + r16) * 128 + 16 * x_chunk(r16, 4 + lg);  // + 2048 f
+  auto read_b = [&](const uint8_t* base, int fm) __attribute__((always_inline)) {
+    const v4i lo = *reinterpret_cast<const v4i*>(base + b_base0 + 2048 * fm);
+    const v4i hi = *reinterpret_cast<const v4i*>(base + b_base1 + 2048 * fm);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto read_a = [&](const uint8_t* base, v4i(&a)[FN], int(&idx)[FN]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int m = m0 + wm * C::TM + fm * 16 + r16;
-    if (m >= M) continue;
-    const float xsm = xs[m];
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int n = n0 + wn * C::TN + fn * 16 + 4 * lg;
-      if (n >= N) continue;
-      store4<OUT>(out, N, m, n, epilogue4(acc[fn][fm], xsm, ws, bias, n));
+    for (int fn = 0; fn < FN; ++fn) {
+      a[fn] = *reinterpret_cast<const v4i*>(base + a_base + 1024 * fn);
+      idx[fn] = *reinterpret_cast<const int*>(base + i_base + 256 * fn);
     }
+  };
+
+  v4f acc[FN][FM];
+
+  // prologue: stages 0..2 in flight, stage 0 landed and visible (KT >= 4)
+#pragma unroll
+  for (int s = 0; s < S; ++s) loader.issue(smem + s * C::STAGE, s);
+  wait_vmcnt<(S - 1) * LPW>();
+  stage_barrier();
+
+  // Two sets of weight fragments, used by alternate steps: the set for step
+  // kt+1 is loaded while step kt's MFMAs read the other, so no register an
+  // MFMA may still be reading is rewritten by an ALU copy.
+  v4i a0[FN], a1[FN];
+  int i0[FN], i1[FN];
+  v8i b[RING];
+  read_a(smem, a0, i0);
+#pragma unroll
+  for (int f = 0; f < PF; ++f) b[f] = read_b(smem, f);
+
+  // The global->LDS loads of one stage are spread over FM positions, at most
+  // two per m block: positions 0 .. FM-SWITCH-1 are m blocks SWITCH .. FM-1 of
+  // step kt (after its barrier), the rest m blocks 0 .. SWITCH-1 of step kt+1,
+  // all before the wait for the stage at step kt+1's barrier.  So the address
+  // unit never queues a whole stage's loads ahead of the wavefront's MFMAs.
+  static_assert((LPW + 1) / 2 <= FM, "issue schedule");
+  auto issue_at = [&](uint8_t* base, int stage, int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 2 * p; j < 2 * p + 2; ++j)
+      if (j < LPW) loader.issue_one(base, stage, j);
+  };
+
+  // One k step on weight set (a, idx), loading set (an, in) for step kt+1.
+  // NEXT: a step kt+1 exists; WAIT: global->LDS loads of this wavefront allowed
+  // to stay pending once stage kt+1 has landed; CONT: finish issuing stage
+  // kt+2 (begun in step kt-1) in m blocks 0 .. SWITCH-1; BEGIN: start issuing
+  // stage kt+3 (into stage kt's slot) at the barrier.
+  auto step = [&](auto next_c, auto wait_c, auto cont_c, auto begin_c, int kt, v4i(&a)[FN], int(&idx)[FN],
+                  v4i(&an)[FN], int(&in)[FN]) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_c)::value, CONT = decltype(cont_c)::value;
+    constexpr bool BEGIN = decltype(begin_c)::value;
+    constexpr int WAIT = decltype(wait_c)::value;
+    const int slot = kt % S, nslot = (kt + 1) % S, pslot = (kt + 2) % S;
+    const uint8_t* cur = smem + slot * C::STAGE;
+    const uint8_t* nxt = smem + nslot * C::STAGE;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if constexpr (CONT) {
+        if (fm < SWITCH) issue_at(smem + pslot * C::STAGE, kt + 2, FM - SWITCH + fm);
+      }
+      if constexpr (NEXT) {
+        if (fm == SWITCH) {
+          wait_vmcnt<WAIT>();
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's reads of stage kt are done
+          stage_barrier();
+          read_a(nxt, an, in);
+        }
+      }
+      if constexpr (BEGIN) {
+        if (fm >= SWITCH) issue_at(smem + slot * C::STAGE, kt + S, fm - SWITCH);
+      }
+      if (fm + PF < FM) b[(fm + PF) % RING] = read_b(cur, fm + PF);
+      else if constexpr (NEXT) b[(fm + PF) % RING] = read_b(nxt, fm + PF - FM);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) smfmac16_acc<XF, WF>(acc[fn][fm], a[fn], b[fm % RING], idx[fn]);
+    }
+  };
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+  // loads a wavefront may leave pending once stage kt+1 has landed: those of
+  // stage kt+2, if it exists
+  using WL = std::integral_constant<int, LPW>;
+  using W0 = std::integral_constant<int, 0>;
+  // The whole step sequence, straight-line for one parity of KT, so that the
+  // fragment set of every step is known at compile time (KT >= 4):
+  //   step 0 begins stage 3; steps 1 .. KT-4 continue and begin stages;
+  //   step KT-3 only continues; steps KT-2 and KT-1 issue nothing.
+  // Accumulator set-up, steps and epilogue all sit inside each parity's path,
+  // so no accumulator is live where the two paths split or join.
+  auto steps = [&](auto odd_c) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_c)::value;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        acc_fence(acc[i][j]);
+      }
+    step(T1{}, WL{}, F0{}, T1{}, 0, a0, i0, a1, i1);
+    int kt = 1;
+    if constexpr (ODD) step(T1{}, WL{}, T1{}, T1{}, kt++, a1, i1, a0, i0);
+    // pairs (kt even when ODD, odd otherwise); KT - 4 - ODD steps remain before step KT-3
+    for (; kt + S + 1 < KT; kt += 2) {
+      if constexpr (ODD) {
+        step(T1{}, WL{}, T1{}, T1{}, kt, a0, i0, a1, i1);
+        step(T1{}, WL{}, T1{}, T1{}, kt + 1, a1, i1, a0, i0);
+      } else {
+        step(T1{}, WL{}, T1{}, T1{}, kt, a1, i1, a0, i0);
+        step(T1{}, WL{}, T1{}, T1{}, kt + 1, a0, i0, a1, i1);
+      }
+    }
+    // kt == KT - 3: odd when KT is even
+    if constexpr (ODD) {
+      step(T1{}, WL{}, T1{}, F0{}, kt, a0, i0, a1, i1);
+      step(T1{}, W0{}, F0{}, F0{}, kt + 1, a1, i1, a0, i0);
+      step(F0{}, W0{}, F0{}, F0{}, kt + 2, a0, i0, a1, i1);
+    } else {
+      step(T1{}, WL{}, T1{}, F0{}, kt, a1, i1, a0, i0);
+      step(T1{}, W0{}, F0{}, F0{}, kt + 1, a0, i0, a1, i1);
+      step(F0{}, W0{}, F0{}, F0{}, kt + 2, a1, i1, a0, i0);
+    }
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc_fence(acc[i][j]);
+    store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg);
+  };
+  if (KT & 1) steps(T1{});
+  else steps(F0{});
+}
+
+template <int XF, int WF, int OUT, int G>
+hipError_t run_wide(const LinearArgs& a, hipStream_t stream) {
+  using C = Tiled<256, 256, 2, 2, 3>;
+  if (a.k < 4 * KSTEP) return hipErrorInvalidValue;  // the step sequence needs K >= 512
+  const int tiles_m = (int)((a.m + 255) / 256), tiles_n = (int)((a.n + 255) / 256);
+  const int T = tiles_m * tiles_n;
+  const int grid = 8 * ((T + 7) / 8);
+  auto kern = linear_wide_kernel<XF, WF, OUT, G>;
+  constexpr int lds = C::LDS;
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
   }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -592,7 +841,10 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t stream) {
   }
   const int64_t big = ((a.m + 255) / 256) * ((a.n + 255) / 256);
   const int64_t mid = ((a.m + 127) / 128) * ((a.n + 127) / 128);
-  if (big >= 512) return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
+  if (big >= 512) {
+    if (a.k >= 4 * KSTEP) return run_wide<XF, WF, OUT, 8>(a, stream);
+    return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
+  }
   if (mid >= 256) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
   return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
 }

@@ -56,4 +56,31 @@ __device__ __forceinline__ v4f smfmac16(v4i a, v8i b, v4f c, int idx) {
     return __builtin_amdgcn_smfmac_f32_16x16x128_bf8_bf8(a, b, c, idx, 0, 0);
 }
 
+// The same instruction through inline assembly, with the accumulator pinned in
+// the accumulation registers (the compiler otherwise may keep a large
+// accumulator set there but select the instruction's VGPR form and copy each
+// accumulator out and back around every MFMA).  volatile keeps these in
+// program order with each other and with memory operations.  The compiler
+// does not see inside the asm, so the two hazards on the accumulator are the
+// caller's: a plain write of it must precede its first MFMA by >= 5 wait
+// states (acc_fence), and its result must not be read sooner than 19 wait
+// states after the MFMA that wrote it (mfma_drain, then acc_fence).
+template <int XF, int WF>
+__device__ __forceinline__ void smfmac16_acc(v4f& c, const v4i& a, const v8i& b, int idx) {
+  if constexpr (WF == FMT_E4M3 && XF == FMT_E4M3)
+    asm volatile("v_smfmac_f32_16x16x128_fp8_fp8 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
+  else if constexpr (WF == FMT_E4M3 && XF == FMT_E5M2)
+    asm volatile("v_smfmac_f32_16x16x128_fp8_bf8 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
+  else if constexpr (WF == FMT_E5M2 && XF == FMT_E4M3)
+    asm volatile("v_smfmac_f32_16x16x128_bf8_fp8 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
+  else
+    asm volatile("v_smfmac_f32_16x16x128_bf8_bf8 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
+}
+
+// Orders every later use of c after this point, 5 wait states on.
+__device__ __forceinline__ void acc_fence(v4f& c) { asm volatile("s_nop 4" : "+a"(c)); }
+
+// 24 wait states: an MFMA issued before this has written its result after it.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
+
 }  // namespace sfr

@@ -175,6 +175,12 @@ RAGGED = [
     sfr_inputs.Case("ragged", 6, 16, 32, 16384, x_fmt=E4, w_fmt=E5),
     sfr_inputs.Case("ragged", 6, 1, 48, 16384, x_fmt=E5, w_fmt=E5, bias=True),
     sfr_inputs.Case("ragged", 6, 7, 96, 2048, x_fmt=E4, w_fmt=E4),
+    # 256 x 256 pipelined kernel (>= 512 tiles, K >= 512): the smallest K, odd
+    # and even step counts with and without the paired main loop, ragged M, N
+    sfr_inputs.Case("ragged", 6, 4100, 8208, 512, x_fmt=E4, w_fmt=E5, bias=True),
+    sfr_inputs.Case("ragged", 6, 4352, 8192, 640, x_fmt=E5, w_fmt=E4),
+    sfr_inputs.Case("ragged", 6, 4096, 8448, 896, x_fmt=E4, w_fmt=E4, bias=True),
+    sfr_inputs.Case("ragged", 6, 4097, 8192, 1280, x_fmt=E5, w_fmt=E5, bias=True),
 ]
 
 
@@ -247,6 +253,11 @@ def test_linear_deterministic(gpu):
     dec = sfr_inputs.Case("det", 7, 7, 4096, 4096, bias=True)
     xb, wb, bb = prepare(dec)
     outs = [host_bf16_bits(gpu_path(gpu, xb, wb, bb, E4, E5)[3]) for _ in range(2)]
+    assert np.array_equal(outs[0], outs[1])
+    wide = sfr_inputs.Case("det", 7, 4096, 8192, 640, bias=True)
+    xb, wb, bb = prepare(wide)
+    say("determinism", wide.name)
+    outs = [host_bf16_bits(gpu_path(gpu, xb, wb, bb, E5, E4)[3]) for _ in range(2)]
     assert np.array_equal(outs[0], outs[1])
 
 
