@@ -61,7 +61,7 @@ def parse():
 # them changes, the stored figure no longer describes the kernel and is not reported.
 TRAFFIC_SOURCES = ("sparse_fp8_row_amd/csrc/gemm.hip", "sparse_fp8_row_amd/csrc/sfr_device.hpp",
                    "sparse_fp8_row_amd/csrc/sfr_launch.hpp")
-TRAFFIC_FILE = "profiles/traffic_linear_tiled_prefill_up.txt"
+TRAFFIC_FILE = "profiles/traffic_linear_wide_prefill_up.txt"
 COPY_BYTES = 1 << 30
 
 
