@@ -73,6 +73,7 @@ def _load():
             "orc_bf16_from_double_array": [P, I64, P],
             "orc_select_array": [P, I64, I, P, P],
             "orc_quantize_rows": [P, I64, I64, I, P, P],
+            "orc_quantize_tensor": [P, I64, I64, I, P, P],
             "orc_compress_2to4": [P, I64, I64, P, P],
             "orc_decompress_2to4": [P, P, I64, I64, P],
             "orc_prune_2to4": [P, I64, I64, P],
@@ -143,6 +144,18 @@ def quantize_rows(x_bf16: np.ndarray, fmt: int):
     q = np.empty((rows, cols), np.uint8)
     s = np.empty(rows, np.float32)
     _load().orc_quantize_rows(_ptr(x), rows, cols, fmt, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_tensor(x_bf16: np.ndarray, fmt: int):
+    """Tensor-wise dynamic FP8 quantization of bf16 bits [rows, cols].
+
+    Returns (q uint8 [rows, cols], scale float32 [1])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(1, np.float32)
+    _load().orc_quantize_tensor(_ptr(x), rows, cols, fmt, _ptr(q), _ptr(s))
     return q, s
 
 

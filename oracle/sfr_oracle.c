@@ -167,6 +167,16 @@ void orc_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
     }
 }
 
+/* Tensor-wise dynamic quantization ([P5]: one scale for the whole tensor, its
+ * amax a deterministic reduction).  It is the row-wise quantization above of
+ * the tensor read as one row of rows*cols elements: a single exact amax, one
+ * scale, the same division and encoding for every element. */
+void orc_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
+                         uint8_t* q, float* scale)
+{
+    orc_quantize_rows(x, 1, rows * cols, fmt, q, scale);
+}
+
 /* ------------------------------------------------------------------------- */
 /* 2:4 selection and compression.  [P1]: converter to the sparse format; the  */
 /* converter must treat -0.0 as zero.                                          */

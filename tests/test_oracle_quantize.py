@@ -1,7 +1,8 @@
 """Pins for the oracle's row-wise FP8 quantization (CPU only).
 
 Checks: hand-derived rows (tests/golden/quantize_rows.txt); an independent
-pipeline built from library routines (numpy binary64 division rounded to
+pipeline built from library routines (for the row-wise and the tensor-wise
+variant) (numpy binary64 division rounded to
 binary32, which equals binary32 division because 53 >= 2*24+2, then torch's
 FP8 cast); the invariants scale*fmax == amax within one binary32 rounding, the
 amax element hitting +/-fmax, the per-element error bound, -0.0 handling, zero
@@ -155,3 +156,69 @@ def test_column_permutation_invariance():
     qp, sp = oracle.quantize_rows(np.ascontiguousarray(x[:, perm]), oracle.E4M3)
     assert np.array_equal(s, sp)
     assert np.array_equal(q[:, perm], qp)
+
+
+# ---- tensor-wise variant: one scale for the whole tensor ----
+
+def independent_tensor_pipeline(x_bits, fmt):
+    """numpy + torch, one amax over every element (no oracle C code)."""
+    xf = oracle.bf16_to_float(x_bits).astype(np.float64)
+    amax = np.max(np.abs(xf))
+    fmax = oracle.FMAX[fmt]
+    if amax == 0:
+        return np.where(np.signbit(xf), 0x80, 0x00).astype(np.uint8), np.zeros(1, np.float32)
+    scale = np.float32(amax / fmax)
+    t = (xf / np.float64(scale)).astype(np.float32)
+    t = np.clip(t, -fmax, fmax)
+    codes = torch.from_numpy(np.ascontiguousarray(t)).to(TORCH_FP8[fmt]).view(torch.uint8).numpy().copy()
+    return codes, np.array([scale], np.float32)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+@pytest.mark.parametrize("kind", ["normal", "student", "wide", "tiny"])
+def test_tensorwise_matches_independent_pipeline(fmt, kind):
+    # "wide" rows differ by up to 2^240 in magnitude: most rows quantize to 0
+    x = _rows(kind, 48, 384, 11 + fmt)
+    q, s = oracle.quantize_tensor(x, fmt)
+    q2, s2 = independent_tensor_pipeline(x, fmt)
+    assert s.shape == (1,)
+    assert np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(q, q2)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_tensorwise_special_cases(fmt):
+    # one row: the same as the row-wise quantization
+    x = _rows("student", 1, 1024, 21)
+    q, s = oracle.quantize_tensor(x, fmt)
+    qr, sr = oracle.quantize_rows(x, fmt)
+    assert np.array_equal(q, qr) and s[0] == sr[0]
+    # the row holding the global amax: its codes equal the row-wise ones; the
+    # global amax element maps to +/-fmax, every other row's codes are those of
+    # its own elements divided by the global scale
+    x = _rows("normal", 16, 256, 22)
+    xf = oracle.bf16_to_float(x)
+    r = int(np.abs(xf).max(axis=1).argmax())
+    q, s = oracle.quantize_tensor(x, fmt)
+    qr, sr = oracle.quantize_rows(x[r:r + 1], fmt)
+    assert s[0] == sr[0] and np.array_equal(q[r], qr[0])
+    assert (q.reshape(-1)[np.abs(xf).argmax()] & 0x7F) == CMAX[fmt]
+    # all-zero tensor: scale 0, signed zeros kept
+    z = np.zeros((3, 64), np.uint16)
+    z[1, ::3] = 0x8000
+    q, s = oracle.quantize_tensor(z, fmt)
+    assert s[0] == 0 and np.array_equal(q, np.where(z == 0x8000, 0x80, 0x00))
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_tensorwise_power_of_two_invariance(fmt):
+    # scaling every element by 2^j (exact in bf16 away from its range limits)
+    # scales amax and scale by 2^j and leaves every code unchanged
+    x = _rows("normal", 24, 256, 23)
+    xf = oracle.bf16_to_float(x).astype(np.float64)
+    q, s = oracle.quantize_tensor(x, fmt)
+    for j in (-20, -3, 5, 40):
+        y = sfr_inputs.to_bf16_bits(xf * 2.0**j)
+        qy, sy = oracle.quantize_tensor(y, fmt)
+        assert np.array_equal(qy, q)
+        assert sy[0] == np.float32(s[0] * np.float32(2.0**j))
