@@ -222,6 +222,7 @@ def main():
         "weight_prep_ms": round(prep_ms, 4),
         "clock_settle_s": SETTLE_S,
     }
+    result["tensorwise"] = bench_tensorwise(torch, sfr, lib, w, x, M, N, K, h, stream)
     del xq, xs, out
 
     if not args.no_decode:
@@ -230,6 +231,50 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def bench_tensorwise(torch, sfr, lib, w, x, M, N, K, h, stream, steps=20, warmup=10):
+    """The same prefill step with tensor-wise scales: quantize_tensorwise_fp8
+    (two launches) + the linear layer with one activation and one weight scale."""
+    pw = sfr.prepare_weight(w, torch.float8_e4m3fn, scaling="tensor")
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    xs = torch.empty((1,), dtype=torch.float32, device=x.device)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    nbytes = int(lib.sfr_quantize_tensorwise_workspace_bytes(M, K))
+    work = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=x.device)
+
+    def quant():
+        st = lib.quantize_tensorwise_fp8(x.data_ptr(), M, K, sfr.SFR_E4M3, xq.data_ptr(), xs.data_ptr(),
+                                         work.data_ptr(), nbytes, h)
+        assert st == 0, st
+
+    def gemm():
+        st = lib.sparse_fp8_scaled_linear(xq.data_ptr(), sfr.SFR_E4M3, xs.data_ptr(), sfr.SFR_SCALE_TENSOR, M, K,
+                                          pw.values.data_ptr(), pw.meta.data_ptr(), sfr.SFR_E4M3, pw.scale.data_ptr(),
+                                          sfr.SFR_SCALE_TENSOR, N, None, out.data_ptr(), sfr.SFR_OUT_BF16, h)
+        assert st == 0, st
+
+    for _ in range(warmup):
+        quant()
+        gemm()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        quant()
+        evs[i][1].record(stream)
+        gemm()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    g_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    print(f"[bench] tensorwise: step {step_ms:.4f} ms (quantize {q_ms:.4f}, gemm {g_ms:.4f})", file=sys.stderr,
+          flush=True)
+    return {"steps": steps, "warmup": warmup, "ms_per_step": round(step_ms, 5),
+            "TFLOP/s": round(2.0 * M * N * K / (step_ms * 1e-3) / 1e12, 2),
+            "kernels_ms": {"quantize_tensorwise": round(q_ms, 5), "gemm": round(g_ms, 5)},
+            "quantize_gbs": round(quant_bytes(M, K) / (q_ms * 1e-3) / 1e9, 1)}
 
 
 def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):

@@ -48,6 +48,11 @@ typedef enum { SFR_E4M3 = 0, SFR_E5M2 = 1 } sfr_fp8_t;
  * before the final bf16 rounding (for accuracy checks). */
 typedef enum { SFR_OUT_BF16 = 0, SFR_OUT_F32 = 1 } sfr_out_t;
 
+/* Scale granularity of one operand of sparse_fp8_scaled_linear: one binary32
+ * scale per row (per token for the activation, per output row for the
+ * weight), or one for the whole operand. */
+typedef enum { SFR_SCALE_ROW = 0, SFR_SCALE_TENSOR = 1 } sfr_scale_t;
+
 typedef enum {
     SFR_OK = 0,
     SFR_ERR_NULL = 1,   /* a required pointer is NULL                         */
@@ -90,6 +95,42 @@ typedef enum {
  */
 sfr_status quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt,
                                 uint8_t* q, float* scale, void* stream);
+
+/*
+ * quantize_tensorwise_fp8 -- dynamic tensor-wise FP8 quantization: the
+ * quantization of quantize_rowwise_fp8 with one scale for the whole tensor
+ * (as if the tensor were a single row of rows*cols elements).  Source:
+ * pytorch/ao PR #1455 ("[float8nocompile] Add alternate Triton kernels for
+ * FP8 conversion which use atomic_max-based algo instead of reduction-based
+ * algo", review thread): tensor-wise FP8 conversion whose global amax must
+ * stay a deterministic reduction.  Here it is computed in two launches --
+ * per-block maxima written to fixed workspace slots, then every block of the
+ * cast kernel reduces all slots itself -- with no atomics; the amax is an
+ * exact integer maximum, so the result is bit-exact and deterministic.
+ *
+ *     amax     = max_{r,k} |x[r, k]|                   (exact)
+ *     scale[0] = fl32(amax / fmax)                     (IEEE binary32 division)
+ *     q[r, k]  = sat_rne_fp8(fl32(x[r, k] / scale[0]))
+ * An all-zero tensor gets scale 0 and sign-keeping zero codes.
+ *
+ *   x          [rows, cols] bf16 bits, device, read.
+ *   dt         format of q.
+ *   q          [rows, cols] FP8 bytes, device, written.
+ *   scale      [1] binary32, device, written.
+ *   workspace  device scratch of at least workspace_bytes =
+ *              sfr_quantize_tensorwise_workspace_bytes(rows, cols) bytes,
+ *              owned by the caller, overwritten; calls that may run at the
+ *              same time need distinct workspaces.
+ * Sizes as quantize_rowwise_fp8.  rows == 0 is a no-op; a workspace smaller
+ * than required is SFR_ERR_SHAPE.
+ */
+sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt,
+                                   uint8_t* q, float* scale, void* workspace, int64_t workspace_bytes,
+                                   void* stream);
+
+/* Workspace bytes quantize_tensorwise_fp8 needs for a [rows, cols] tensor
+ * (at most 2 KB); 0 for sizes it rejects. */
+int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
  * compress_2to4_fp8 -- 2:4 semi-structured compression of an FP8 matrix.
@@ -147,6 +188,22 @@ sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const fl
                                      const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
                                      const float* ws, int64_t n, const uint16_t* bias,
                                      void* out, sfr_out_t out_dt, void* stream);
+
+/*
+ * sparse_fp8_scaled_linear -- sparse_fp8_rowwise_linear with the scale
+ * granularity of each operand chosen: xs_kind / ws_kind SFR_SCALE_ROW reads
+ * xs[m] / ws[n] as above, SFR_SCALE_TENSOR reads the single xs[0] / ws[0] for
+ * every row (the tensor-wise scaling of quantize_tensorwise_fp8).  Everything
+ * else -- arguments, sizes, accumulation, epilogue, errors -- is as
+ * sparse_fp8_rowwise_linear, which is this call with both kinds
+ * SFR_SCALE_ROW.  An unknown kind is SFR_ERR_DTYPE.
+ */
+sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs,
+                                    sfr_scale_t xs_kind, int64_t m, int64_t k,
+                                    const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                    const float* ws, sfr_scale_t ws_kind, int64_t n,
+                                    const uint16_t* bias, void* out, sfr_out_t out_dt,
+                                    void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sfr_status_string(sfr_status s);

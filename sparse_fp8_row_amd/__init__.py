@@ -9,6 +9,9 @@ device memory and the current HIP stream.
     w = prepare_weight(w_bf16, torch.float8_e4m3fn)     # once per weight
     y = sparse_fp8_rowwise_linear(xq, xs, w.values, w.meta, w.scale, bias)
 
+Tensor-wise scaling (one scale per operand): ``quantize_tensorwise_fp8``,
+``prepare_weight(..., scaling="tensor")`` and ``sparse_fp8_scaled_linear``.
+
 The operator follows pytorch/ao PR #1671 ("Add CUTLASS-based row-wise scaled
 sparse FP8 kernel"); see the header for the exact contract of each call.
 There is no fallback: if the library is missing or no GPU is present the
@@ -28,9 +31,11 @@ LIB_PATH = os.path.join(HERE, "libsparse_fp8_row.so")
 
 SFR_E4M3, SFR_E5M2 = 0, 1
 SFR_OUT_BF16, SFR_OUT_F32 = 0, 1
+SFR_SCALE_ROW, SFR_SCALE_TENSOR = 0, 1
 STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN",
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
-EXPORTED = ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear",
+EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
+            "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
             "sfr_status_string", "sfr_format_version")
 
 _FP8 = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
@@ -55,8 +60,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quantize_rowwise_fp8.argtypes = [P, I64, I64, I, P, P, P]
     lib.compress_2to4_fp8.argtypes = [P, I64, I64, I, P, P, P]
     lib.sparse_fp8_rowwise_linear.argtypes = [P, I, P, I64, I64, P, P, I, P, I64, P, P, I, P]
-    for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear):
+    lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
+    lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
+    for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
+               lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear):
         fn.restype = I
+    lib.sfr_quantize_tensorwise_workspace_bytes.argtypes = [I64, I64]
+    lib.sfr_quantize_tensorwise_workspace_bytes.restype = I64
     lib.sfr_status_string.argtypes = [I]
     lib.sfr_status_string.restype = ctypes.c_char_p
     lib.sfr_format_version.argtypes = []
@@ -102,6 +112,22 @@ def quantize_rowwise_fp8(x: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None
     return q, s
 
 
+def quantize_tensorwise_fp8(x: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None):
+    """bf16 [rows, cols] -> (q FP8 [rows, cols], scale float32 [1]): one scale for the tensor."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    lib = load()
+    q = torch.empty((rows, cols), dtype=dtype, device=x.device)
+    s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    nbytes = max(int(lib.sfr_quantize_tensorwise_workspace_bytes(rows, cols)), 16)
+    work = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    _check(lib.quantize_tensorwise_fp8(x.data_ptr(), rows, cols, _fp8_enum(dtype), q.data_ptr(), s.data_ptr(),
+                                       work.data_ptr(), nbytes, _stream(stream)), "quantize_tensorwise_fp8")
+    return q, s
+
+
 def compress_2to4_fp8(wq: torch.Tensor, stream=None):
     """FP8 [n, k] -> (values FP8 [n, k/2], meta uint8 [n, k/8])."""
     _dev(wq, "wq")
@@ -111,6 +137,41 @@ def compress_2to4_fp8(wq: torch.Tensor, stream=None):
     _check(load().compress_2to4_fp8(wq.data_ptr(), n, k, _fp8_enum(wq.dtype), values.data_ptr(),
                                     meta.data_ptr(), _stream(stream)), "compress_2to4_fp8")
     return values, meta
+
+
+def sparse_fp8_scaled_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.Tensor, meta: torch.Tensor,
+                             ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                             out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+    """out[m, n] = xs * ws * sum_k xq[m, k] * wq[n, k] (+ bias[n]), as bf16 (or float32).
+
+    Each scale is per row (xs [m], ws [n]) or one for the tensor (shape [1]);
+    the granularity follows from the scale's length."""
+    for t, nm in ((xq, "xq"), (xs, "xs"), (values, "values"), (meta, "meta"), (ws, "ws")):
+        _dev(t, nm)
+    m, k = xq.shape
+    n = values.shape[0]
+    if values.shape != (n, k // 2) or meta.shape != (n, k // 8):
+        raise ValueError("operand shapes do not match")
+    if xs.dim() != 1 or ws.dim() != 1 or xs.dtype != torch.float32 or ws.dtype != torch.float32:
+        raise ValueError("scales must be 1-D float32")
+    xk = SFR_SCALE_ROW if xs.shape[0] == m and m != 1 else SFR_SCALE_TENSOR if xs.shape[0] == 1 else None
+    wk = SFR_SCALE_ROW if ws.shape[0] == n and n != 1 else SFR_SCALE_TENSOR if ws.shape[0] == 1 else None
+    if xk is None or wk is None:
+        raise ValueError("scales must have one entry per row or a single entry")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.shape != (n,):
+            raise ValueError("bias must be bfloat16 [n]")
+    od = {torch.bfloat16: SFR_OUT_BF16, torch.float32: SFR_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=xq.device)
+    elif out.shape != (m, n) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(load().sparse_fp8_scaled_linear(
+        xq.data_ptr(), _fp8_enum(xq.dtype), xs.data_ptr(), xk, m, k, values.data_ptr(), meta.data_ptr(),
+        _fp8_enum(values.dtype), ws.data_ptr(), wk, n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od,
+        _stream(stream)), "sparse_fp8_scaled_linear")
+    return out
 
 
 def sparse_fp8_rowwise_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.Tensor, meta: torch.Tensor,
@@ -150,19 +211,31 @@ class SparseFp8Weight:
     format_version: int = 1
 
 
-def prepare_weight(w: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None) -> SparseFp8Weight:
-    """bf16 weight [N, K] -> row-wise FP8 quantization, then 2:4 compression.
+def prepare_weight(w: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None, scaling: str = "row") -> SparseFp8Weight:
+    """bf16 weight [N, K] -> FP8 quantization (row-wise, or tensor-wise with
+    scaling="tensor"), then 2:4 compression.
 
     The compressor keeps the two largest FP8 magnitudes of every group of four,
-    which is the 2:4 magnitude pruning; the row scale is unaffected by it because
+    which is the 2:4 magnitude pruning; the scale is unaffected by it because
     a row's largest element is always kept."""
-    wq, ws = quantize_rowwise_fp8(w, dtype, stream)
+    if scaling == "row":
+        wq, ws = quantize_rowwise_fp8(w, dtype, stream)
+    elif scaling == "tensor":
+        wq, ws = quantize_tensorwise_fp8(w, dtype, stream)
+    else:
+        raise ValueError("scaling must be 'row' or 'tensor'")
     values, meta = compress_2to4_fp8(wq, stream)
     return SparseFp8Weight(values, meta, ws, int(load().sfr_format_version()))
 
 
 def linear(x: torch.Tensor, w: SparseFp8Weight, bias: Optional[torch.Tensor] = None,
-           act_dtype=torch.float8_e4m3fn, stream=None) -> torch.Tensor:
-    """bf16 x [M, K] -> bf16 [M, N]: dynamic activation quantization + sparse FP8 GEMM."""
-    xq, xs = quantize_rowwise_fp8(x, act_dtype, stream)
-    return sparse_fp8_rowwise_linear(xq, xs, w.values, w.meta, w.scale, bias, stream=stream)
+           act_dtype=torch.float8_e4m3fn, stream=None, act_scaling: str = "row") -> torch.Tensor:
+    """bf16 x [M, K] -> bf16 [M, N]: dynamic activation quantization (row- or
+    tensor-wise) + sparse FP8 GEMM."""
+    if act_scaling == "row":
+        xq, xs = quantize_rowwise_fp8(x, act_dtype, stream)
+    elif act_scaling == "tensor":
+        xq, xs = quantize_tensorwise_fp8(x, act_dtype, stream)
+    else:
+        raise ValueError("act_scaling must be 'row' or 'tensor'")
+    return sparse_fp8_scaled_linear(xq, xs, w.values, w.meta, w.scale, bias, stream=stream)

@@ -9,6 +9,7 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool fp8_ok(int dt) { return dt == SFR_E4M3 || dt == SFR_E5M2; }
+bool scale_ok(int kind) { return kind == SFR_SCALE_ROW || kind == SFR_SCALE_TENSOR; }
 // Bound on rows * cols of any one tensor, keeping every grid within HIP's limits.
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
@@ -30,6 +31,26 @@ sfr_status quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, s
   return launch_status(sfr::launch_quantize(x, rows, cols, dt, q, scale, static_cast<hipStream_t>(stream)));
 }
 
+int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || rows > SFR_MAX_DIM || cols <= 0 || cols > SFR_MAX_DIM || cols % 8 != 0 || rows * cols > kMaxElems)
+    return 0;
+  return sfr::tensor_workspace_bytes(rows, cols);
+}
+
+sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt, uint8_t* q,
+                                   float* scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!fp8_ok(dt)) return SFR_ERR_DTYPE;
+  if (rows < 0 || rows > SFR_MAX_DIM || cols <= 0 || cols > SFR_MAX_DIM || cols % 8 != 0 ||
+      rows * cols > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (rows == 0) return SFR_OK;
+  if (workspace_bytes < sfr::tensor_workspace_bytes(rows, cols)) return SFR_ERR_SHAPE;
+  if (!x || !q || !scale || !workspace) return SFR_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale) || !aligned16(workspace)) return SFR_ERR_ALIGN;
+  return launch_status(
+      sfr::launch_quantize_tensor(x, rows, cols, dt, q, scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
 sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t dt, uint8_t* values, uint8_t* meta,
                              void* stream) {
   if (!fp8_ok(dt)) return SFR_ERR_DTYPE;
@@ -41,10 +62,13 @@ sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t d
   return launch_status(sfr::launch_compress(w, n, k, values, meta, static_cast<hipStream_t>(stream)));
 }
 
-sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs, int64_t m, int64_t k,
-                                     const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt, const float* ws,
-                                     int64_t n, const uint16_t* bias, void* out, sfr_out_t out_dt, void* stream) {
-  if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32)) return SFR_ERR_DTYPE;
+sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs, sfr_scale_t xs_kind, int64_t m,
+                                    int64_t k, const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                    const float* ws, sfr_scale_t ws_kind, int64_t n, const uint16_t* bias, void* out,
+                                    sfr_out_t out_dt, void* stream) {
+  if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32) || !scale_ok(xs_kind) ||
+      !scale_ok(ws_kind))
+    return SFR_ERR_DTYPE;
   if (m < 0 || m > SFR_MAX_DIM || n < 0 || n > SFR_MAX_DIM || n % 16 != 0 || k <= 0 || k > SFR_MAX_DIM ||
       k % 128 != 0 || m * k > kMaxElems || n * k > kMaxElems || m * n > kMaxElems)
     return SFR_ERR_SHAPE;
@@ -53,8 +77,16 @@ sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const fl
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(values) || !aligned16(meta) || !aligned16(ws) ||
       !aligned16(out) || (bias && !aligned16(bias)))
     return SFR_ERR_ALIGN;
-  sfr::LinearArgs a{xq, xs, values, meta, ws, bias, out, m, n, k, (int)x_dt, (int)w_dt, (int)out_dt};
+  sfr::LinearArgs a{xq, xs, values, meta, ws, bias, out, m, n, k, (int)x_dt, (int)w_dt, (int)out_dt,
+                    xs_kind == SFR_SCALE_ROW ? 1 : 0, ws_kind == SFR_SCALE_ROW ? 1 : 0};
   return launch_status(sfr::launch_linear(a, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs, int64_t m, int64_t k,
+                                     const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt, const float* ws,
+                                     int64_t n, const uint16_t* bias, void* out, sfr_out_t out_dt, void* stream) {
+  return sparse_fp8_scaled_linear(xq, x_dt, xs, SFR_SCALE_ROW, m, k, values, meta, w_dt, ws, SFR_SCALE_ROW, n, bias,
+                                  out, out_dt, stream);
 }
 
 const char* sfr_status_string(sfr_status s) {

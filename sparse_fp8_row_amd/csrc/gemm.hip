@@ -61,6 +61,13 @@ __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t
   }
 }
 
+// Weight scales of outputs n .. n+3: four row scales, or the one tensor scale.
+__device__ __forceinline__ v4f load_ws4(const float* __restrict__ ws, int n, int ws_stride) {
+  if (ws_stride) return *reinterpret_cast<const v4f*>(ws + n);
+  const float w = ws[0];
+  return v4f{w, w, w, w};
+}
+
 // Epilogue of a wavefront's FN x FM grid of 16x16 blocks (block (fn, fm) at
 // rows nb + 16 fn, columns mb + 16 fm of the product; lane (r16, lg) holds
 // n = 4 lg .. 4 lg + 3 of column m = r16).  Every scale and bias load is
@@ -70,16 +77,17 @@ __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t
 template <int OUT, int FN, int FM>
 __device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float* __restrict__ xs,
                                            const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-                                           void* __restrict__ out, int M, int N, int mb, int nb, int r16, int lg) {
+                                           void* __restrict__ out, int M, int N, int mb, int nb, int r16, int lg,
+                                           int xs_stride, int ws_stride) {
   float xsv[FM];
   v4f wsv[FN];
   uint2 bv[FN];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) xsv[fm] = xs[min(mb + fm * 16 + r16, M - 1)];
+  for (int fm = 0; fm < FM; ++fm) xsv[fm] = xs[min(mb + fm * 16 + r16, M - 1) * xs_stride];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int nc = min(nb + fn * 16 + 4 * lg, N - 4);
-    wsv[fn] = *reinterpret_cast<const v4f*>(ws + nc);
+    wsv[fn] = load_ws4(ws, nc, ws_stride);
     bv[fn] = bias ? *reinterpret_cast<const uint2*>(bias + nc) : make_uint2(0u, 0u);
   }
 #pragma unroll
@@ -230,7 +238,7 @@ template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S,
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-    void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
+    void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
   using C = Tiled<BN, BM, WN, WM, S>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   }
 
   // ---- epilogue: scales, bias, bf16, store ----
-  store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg);
+  store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +369,7 @@ template <int XF, int WF, int OUT, int G>
 __global__ __launch_bounds__(256, 1) void linear_wide_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-    void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
+    void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
   constexpr int BN = 256, BM = 256, S = 3;
   using C = Tiled<BN, BM, 2, 2, S>;
   using L = StageLoader<BN, BM, C::NW>;
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc_fence(acc[i][j]);
-    store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg);
+    store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
   };
   if (KT & 1) steps(T1{});
   else steps(F0{});
@@ -548,7 +556,7 @@ hipError_t run_wide(const LinearArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n);
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride, a.ws_stride);
   return hipGetLastError();
 }
 
@@ -563,7 +571,7 @@ template <int XF, int WF, int OUT, int NWV, int U, bool NT = true>
 __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-    void* __restrict__ out, int M, int N, int K) {
+    void* __restrict__ out, int M, int N, int K, int xs_stride, int ws_stride) {
   __shared__ v4f red[NWV][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -583,8 +591,8 @@ __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
   v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
   uint2 b2 = make_uint2(0, 0);
   if (wave == 0) {
-    xsm = xs[min(m, M - 1)];
-    w4 = *reinterpret_cast<const v4f*>(ws + n);
+    xsm = xs[min(m, M - 1) * xs_stride];
+    w4 = load_ws4(ws, n, ws_stride);
     if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
   }
 
@@ -650,7 +658,7 @@ template <int XF, int WF, int OUT, bool XL>
 __global__ __launch_bounds__(256) void linear_decode_lds_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-    void* __restrict__ out, int M, int N, int K) {
+    void* __restrict__ out, int M, int N, int K, int xs_stride, int ws_stride) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -668,8 +676,8 @@ __global__ __launch_bounds__(256) void linear_decode_lds_kernel(
   v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
   uint2 b2 = make_uint2(0, 0);
   if (wave == 0) {
-    xsm = xs[min(m, M - 1)];
-    w4 = *reinterpret_cast<const v4f*>(ws + n);
+    xsm = xs[min(m, M - 1) * xs_stride];
+    w4 = load_ws4(ws, n, ws_stride);
     if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
   }
   // stream the block into LDS: LDS chunk p holds global chunk p ^ (row(p) & 7)
@@ -800,7 +808,7 @@ hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n);
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride, a.ws_stride);
   return hipGetLastError();
 }
 
@@ -822,14 +830,14 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t stream) {
         attr_set[xl] = true;
       }
       hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(256), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                         a.bias, a.out, (int)a.m, (int)a.n, (int)a.k);
+                         a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
       return hipGetLastError();
     }
     const int64_t kt = a.k / KSTEP;
     const dim3 grid((unsigned)(a.n / 16));
 #define SFR_DEC(NWV, U)                                                                                      \
   hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT, NWV, U>), grid, dim3(64 * NWV), 0, stream, a.xq, a.xs, \
-                     a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k)
+                     a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride)
     if (kt <= 8) SFR_DEC(8, 1);
     else if (kt <= 16) SFR_DEC(8, 2);
     else if (kt <= 32) SFR_DEC(8, 4);

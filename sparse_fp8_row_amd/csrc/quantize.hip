@@ -195,7 +195,109 @@ hipError_t launch_fmt(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Tensor-wise variant: one scale for the whole tensor.  Two launches over the
+// same split of the tensor into blocks of `per_block` 16-byte chunks: the
+// first writes each block's magnitude maximum to its own workspace slot; the
+// second has every block reduce all slots (the same exact integer max in every
+// block, no atomics, so the result is deterministic by construction), derive
+// the scale and cast its chunks exactly as the row-wise kernel does.
+// ---------------------------------------------------------------------------
+constexpr int kTensorThreads = 256;
+constexpr int64_t kTensorMaxBlocks = 512;
+
+// chunks per block: a multiple of the block size, at most kTensorMaxBlocks blocks
+__host__ __device__ inline int64_t tensor_chunks_per_block(int64_t chunks) {
+  int64_t per = (chunks + kTensorMaxBlocks - 1) / kTensorMaxBlocks;
+  per = (per + kTensorThreads - 1) / kTensorThreads * kTensorThreads;
+  return per < kTensorThreads ? kTensorThreads : per;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
+  m = wave_max(m);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < kTensorThreads / 64; ++w) r = max(r, red[w]);
+  return r;
+}
+
+__global__ __launch_bounds__(kTensorThreads) void tensor_amax_kernel(const uint4* __restrict__ x, int64_t chunks,
+                                                                     int64_t per_block, uint32_t* __restrict__ part) {
+  __shared__ uint32_t red[kTensorThreads / 64];
+  const int64_t c0 = (int64_t)blockIdx.x * per_block;
+  const int64_t c1 = min(c0 + per_block, chunks);
+  uint32_t m = 0;
+  int64_t c = c0 + threadIdx.x;
+  // four loads in flight per thread
+  for (; c + 3 * kTensorThreads < c1; c += 4 * kTensorThreads) {
+    const uint4 v0 = x[c], v1 = x[c + kTensorThreads], v2 = x[c + 2 * kTensorThreads], v3 = x[c + 3 * kTensorThreads];
+    m = mag_max8(v0, m);
+    m = mag_max8(v1, m);
+    m = mag_max8(v2, m);
+    m = mag_max8(v3, m);
+  }
+  for (; c < c1; c += kTensorThreads) m = mag_max8(x[c], m);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kTensorThreads) void tensor_cast_kernel(const uint4* __restrict__ x, int64_t chunks,
+                                                                     int64_t per_block,
+                                                                     const uint32_t* __restrict__ part, int nparts,
+                                                                     uint2* __restrict__ q, float* __restrict__ scale) {
+  __shared__ uint32_t red[kTensorThreads / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kTensorThreads) m = max(m, part[i]);
+  m = block_max(m, red);
+  const float amax = bf16_to_f32(m);
+  const float s = amax / Fp8<FMT>::fmax;
+  const float r = 1.0f / s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = (m == 0) ? 0.0f : s;
+  const int64_t c0 = (int64_t)blockIdx.x * per_block;
+  const int64_t c1 = min(c0 + per_block, chunks);
+  if (m == 0) {
+    for (int64_t c = c0 + threadIdx.x; c < c1; c += kTensorThreads) q[c] = zero8(x[c]);
+    return;
+  }
+  int64_t c = c0 + threadIdx.x;
+  for (; c + 3 * kTensorThreads < c1; c += 4 * kTensorThreads) {
+    const uint4 v0 = x[c], v1 = x[c + kTensorThreads], v2 = x[c + 2 * kTensorThreads], v3 = x[c + 3 * kTensorThreads];
+    q[c] = cast8<FMT>(v0, s, r);
+    q[c + kTensorThreads] = cast8<FMT>(v1, s, r);
+    q[c + 2 * kTensorThreads] = cast8<FMT>(v2, s, r);
+    q[c + 3 * kTensorThreads] = cast8<FMT>(v3, s, r);
+  }
+  for (; c < c1; c += kTensorThreads) q[c] = cast8<FMT>(x[c], s, r);
+}
+
 }  // namespace
+
+int64_t tensor_workspace_bytes(int64_t rows, int64_t cols) {
+  const int64_t chunks = rows * cols / 8;
+  const int64_t per = tensor_chunks_per_block(chunks);
+  return 4 * ((chunks + per - 1) / per);
+}
+
+hipError_t launch_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* scale,
+                                  void* workspace, hipStream_t stream) {
+  const int64_t chunks = rows * cols / 8;
+  const int64_t per = tensor_chunks_per_block(chunks);
+  const int nb = (int)((chunks + per - 1) / per);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint32_t* part = static_cast<uint32_t*>(workspace);
+  hipLaunchKernelGGL(tensor_amax_kernel, dim3(nb), dim3(kTensorThreads), 0, stream, xv, chunks, per, part);
+  if (fmt == FMT_E4M3)
+    hipLaunchKernelGGL(tensor_cast_kernel<FMT_E4M3>, dim3(nb), dim3(kTensorThreads), 0, stream, xv, chunks, per, part,
+                       nb, reinterpret_cast<uint2*>(q), scale);
+  else
+    hipLaunchKernelGGL(tensor_cast_kernel<FMT_E5M2>, dim3(nb), dim3(kTensorThreads), 0, stream, xv, chunks, per, part,
+                       nb, reinterpret_cast<uint2*>(q), scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
                            float* scale, hipStream_t stream) {

@@ -29,6 +29,8 @@ asserted to stay below 1e-3 (measured: none on normal data at K=4096; 2 in
 from __future__ import annotations
 
 import numpy as np
+
+import sfr_inputs
 import torch
 
 import oracle
@@ -132,3 +134,24 @@ def check_bf16(bits_gpu: np.ndarray, ref: dict, hwb: np.ndarray) -> dict:
             "strict_misses": int(strict.sum()),
             "strict_rate_ok": bool(strict.sum() <= max(1, STRICT_MISS_RATE * y.size)),
             "first_bad": None if not bad.any() else np.argwhere(bad)[0].tolist()}
+
+
+# Quantization test rows: bf16 bits [rows, cols] of one of four value
+# families, with 2% exact signed zeros and (rows > 2) an all-zero row 1.
+def rows_bits(kind, rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        x = rng.standard_normal((rows, cols))
+    elif kind == "student":
+        x = rng.standard_t(3.0, (rows, cols))
+        x[:, rng.choice(cols, max(1, cols // 100), replace=False)] *= 50
+    elif kind == "wide":
+        x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-120, 120, (rows, 1)))
+    elif kind == "tiny":
+        x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-133, -118, (rows, 1)))
+    bits = sfr_inputs.to_bf16_bits(x)
+    z = rng.random((rows, cols)) < 0.02
+    bits[z] = np.where(rng.random(int(z.sum())) < 0.5, 0x8000, 0x0000)
+    if rows > 2:
+        bits[1] = np.where(rng.random(cols) < 0.5, 0x8000, 0x0000)   # an all-zero row
+    return bits

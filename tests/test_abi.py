@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
-              "sfr_format_version"):
+              "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
+              "sparse_fp8_scaled_linear"):
         assert n in names
 
 
@@ -99,6 +100,44 @@ def test_linear_validation(lib):
     assert call(ws=U) == ALIGN
     assert call(bias=U) == ALIGN
     assert call(out=U) == ALIGN
+
+
+def test_tensorwise_quantize_validation(lib):
+    wb = lib.sfr_quantize_tensorwise_workspace_bytes
+    assert wb(8192, 4096) == 2048                       # 512 blocks of 8192 chunks
+    assert wb(16, 4096) == 4 * (16 * 4096 // 8 // 256)  # blocks of 256 chunks
+    assert wb(1, 8) == 4
+    assert wb(4, 15) == 0 and wb(0, 16) == 0 and wb(-1, 16) == 0
+    q = lib.quantize_tensorwise_fp8
+    need = wb(4, 16)
+    assert q(A, 4, 16, 2, A, A, A, need, None) == DTYPE
+    assert q(A, 4, 15, 0, A, A, A, need, None) == SHAPE
+    assert q(A, 4, 0, 0, A, A, A, need, None) == SHAPE
+    assert q(A, 4, 16, 0, A, A, A, need - 1, None) == SHAPE    # workspace too small
+    assert q(None, 0, 16, 0, None, None, None, 0, None) == OK   # empty: no-op
+    assert q(None, 4, 16, 0, A, A, A, need, None) == NULL
+    assert q(A, 4, 16, 0, A, A, None, need, None) == NULL
+    assert q(A, 4, 16, 0, A, U, A, need, None) == ALIGN
+    assert q(A, 4, 16, 0, A, A, U, need, None) == ALIGN
+
+
+def test_scaled_linear_validation(lib):
+    f = lib.sparse_fp8_scaled_linear
+    good = dict(xq=A, xd=0, xs=A, xk=0, m=4, k=256, v=A, meta=A, wd=0, ws=A, wk=1, n=32, bias=None, out=A, od=0)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["xq"], a["xd"], a["xs"], a["xk"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["wk"],
+                 a["n"], a["bias"], a["out"], a["od"], None)
+
+    assert call(xk=2) == DTYPE
+    assert call(wk=-1) == DTYPE
+    assert call(xd=3) == DTYPE
+    assert call(k=192) == SHAPE
+    assert call(n=8) == SHAPE
+    assert call(m=0, xq=None, xs=None, out=None) == OK
+    assert call(xs=None) == NULL
+    assert call(ws=U) == ALIGN
 
 
 def test_binding_rejects_host_tensors():

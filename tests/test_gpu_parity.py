@@ -16,7 +16,7 @@ import torch
 import oracle
 import sfr_inputs
 from parity import (check_bf16, check_f32, dev_bf16, dev_fp8, host_bf16_bits, host_bytes, host_f32, hw_bound,
-                    FP8_TORCH)
+                    rows_bits, FP8_TORCH)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,25 +35,6 @@ def gpu():
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def rows_bits(kind, rows, cols, seed):
-    rng = np.random.default_rng(seed)
-    if kind == "normal":
-        x = rng.standard_normal((rows, cols))
-    elif kind == "student":
-        x = rng.standard_t(3.0, (rows, cols))
-        x[:, rng.choice(cols, max(1, cols // 100), replace=False)] *= 50
-    elif kind == "wide":
-        x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-120, 120, (rows, 1)))
-    elif kind == "tiny":
-        x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-133, -118, (rows, 1)))
-    bits = sfr_inputs.to_bf16_bits(x)
-    z = rng.random((rows, cols)) < 0.02
-    bits[z] = np.where(rng.random(int(z.sum())) < 0.5, 0x8000, 0x0000)
-    if rows > 2:
-        bits[1] = np.where(rng.random(cols) < 0.5, 0x8000, 0x0000)   # an all-zero row
-    return bits
 
 
 # ---------------------------------------------------------------------------
