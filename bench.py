@@ -322,6 +322,40 @@ def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
         res[f"M{m}"] = {"us_per_call": round(us, 3), "bytes": b, "GB/s": round(gbs, 1),
                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         print(f"[bench] decode M={m}: {us:.3f} us/call, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+        # the layer from the bf16 activation: quantization + GEMM as two
+        # launches, and fused into one (sparse_fp8_rowwise_linear_dynamic)
+        xq2 = torch.empty_like(xq)
+        xs2 = torch.empty_like(xs)
+
+        def two(i):
+            st = lib.quantize_rowwise_fp8(x.data_ptr(), m, k, sfr.SFR_E4M3, xq2.data_ptr(), xs2.data_ptr(), h)
+            assert st == 0, st
+            st = lib.sparse_fp8_rowwise_linear(xq2.data_ptr(), sfr.SFR_E4M3, xs2.data_ptr(), m, k,
+                                               vals[i].data_ptr(), metas[i].data_ptr(), sfr.SFR_E4M3,
+                                               base.scale.data_ptr(), n, bias.data_ptr(), out.data_ptr(),
+                                               sfr.SFR_OUT_BF16, h)
+            assert st == 0, st
+
+        def fused(i):
+            st = lib.sparse_fp8_rowwise_linear_dynamic(x.data_ptr(), sfr.SFR_E4M3, m, k, vals[i].data_ptr(),
+                                                       metas[i].data_ptr(), sfr.SFR_E4M3, base.scale.data_ptr(),
+                                                       sfr.SFR_SCALE_ROW, n, bias.data_ptr(), out.data_ptr(),
+                                                       sfr.SFR_OUT_BF16, xq2.data_ptr(), xs2.data_ptr(), h)
+            assert st == 0, st
+
+        for name, fn in (("quantize_plus_gemm", two), ("fused", fused)):
+            for i in range(copies):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                fn(i % copies)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e3 / reps
+            res[f"M{m}"][f"{name}_us_per_call"] = round(t, 3)
+            print(f"[bench] decode M={m} from bf16, {name}: {t:.3f} us/call", file=sys.stderr, flush=True)
     return res
 
 

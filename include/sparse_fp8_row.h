@@ -205,6 +205,31 @@ sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const flo
                                     const uint16_t* bias, void* out, sfr_out_t out_dt,
                                     void* stream);
 
+/*
+ * sparse_fp8_rowwise_linear_dynamic -- the layer from the bf16 activation:
+ * quantize_rowwise_fp8 of x into (xq, xs), then sparse_fp8_scaled_linear with
+ * row activation scales.  Source: PR #1671, item 4 (the activation is
+ * quantized dynamically, per call).  xq and xs receive exactly the bytes
+ * quantize_rowwise_fp8 writes; out is as sparse_fp8_scaled_linear.
+ *
+ * For the smallest decode shapes -- k 2048 or 4096 and m * k <= 4096 -- both
+ * steps run in ONE launch: every workgroup quantizes the activation itself
+ * into its on-chip operand stage (no workgroup waits for another).  Other
+ * shapes take two launches (quantization, then the linear layer), which is
+ * faster once the activation is larger.
+ *
+ *   x      [m, k] bf16 bits, device, read.
+ *   xq     [m, k] FP8 bytes (format x_dt), device, written.
+ *   xs     [m] binary32, device, written.
+ * Other arguments, sizes and errors as sparse_fp8_scaled_linear (ws_kind
+ * selects row or tensor weight scales).
+ */
+sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, int64_t m, int64_t k,
+                                             const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                             const float* ws, sfr_scale_t ws_kind, int64_t n,
+                                             const uint16_t* bias, void* out, sfr_out_t out_dt,
+                                             uint8_t* xq, float* xs, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sfr_status_string(sfr_status s);
 

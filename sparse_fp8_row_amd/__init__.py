@@ -36,6 +36,7 @@ STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN"
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
 EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
             "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
+            "sparse_fp8_rowwise_linear_dynamic",
             "sfr_status_string", "sfr_format_version")
 
 _FP8 = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
@@ -62,8 +63,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_fp8_rowwise_linear.argtypes = [P, I, P, I64, I64, P, P, I, P, I64, P, P, I, P]
     lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
     lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
+    lib.sparse_fp8_rowwise_linear_dynamic.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, P]
     for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
-               lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear):
+               lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic):
         fn.restype = I
     lib.sfr_quantize_tensorwise_workspace_bytes.argtypes = [I64, I64]
     lib.sfr_quantize_tensorwise_workspace_bytes.restype = I64
@@ -200,6 +202,40 @@ def sparse_fp8_rowwise_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.
         _fp8_enum(values.dtype), ws.data_ptr(), n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od,
         _stream(stream)), "sparse_fp8_rowwise_linear")
     return out
+
+
+def sparse_fp8_rowwise_linear_dynamic(x: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, ws: torch.Tensor,
+                                      bias: Optional[torch.Tensor] = None, act_dtype=torch.float8_e4m3fn,
+                                      out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+    """bf16 x [m, k] -> (out [m, n], xq [m, k], xs [m]): row-wise activation
+    quantization and the linear layer, fused into one launch for small decode shapes."""
+    for t, nm in ((x, "x"), (values, "values"), (meta, "meta"), (ws, "ws")):
+        _dev(t, nm)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    m, k = x.shape
+    n = values.shape[0]
+    if values.shape != (n, k // 2) or meta.shape != (n, k // 8) or ws.dim() != 1:
+        raise ValueError("operand shapes do not match")
+    wk = SFR_SCALE_ROW if ws.shape[0] == n and n != 1 else SFR_SCALE_TENSOR if ws.shape[0] == 1 else None
+    if wk is None or ws.dtype != torch.float32:
+        raise ValueError("ws must be float32 [n] or [1]")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.shape != (n,):
+            raise ValueError("bias must be bfloat16 [n]")
+    od = {torch.bfloat16: SFR_OUT_BF16, torch.float32: SFR_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    elif out.shape != (m, n) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    xq = torch.empty((m, k), dtype=act_dtype, device=x.device)
+    xs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(load().sparse_fp8_rowwise_linear_dynamic(
+        x.data_ptr(), _fp8_enum(act_dtype), m, k, values.data_ptr(), meta.data_ptr(), _fp8_enum(values.dtype),
+        ws.data_ptr(), wk, n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od, xq.data_ptr(),
+        xs.data_ptr(), _stream(stream)), "sparse_fp8_rowwise_linear_dynamic")
+    return out, xq, xs
 
 
 @dataclass

@@ -20,99 +20,12 @@
 // row again (from L2 in practice).
 #include "sfr_device.hpp"
 #include "sfr_launch.hpp"
+#include "sfr_quant.hpp"
 
 namespace sfr {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // 4 wavefronts of 64 lanes
-
-__device__ __forceinline__ uint32_t mag_max8(uint4 c, uint32_t m) {
-  // |bf16| order == unsigned order of the low 15 bits (finite inputs)
-  uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = max(m, w[i] & 0x7FFFu);
-    m = max(m, (w[i] >> 16) & 0x7FFFu);
-  }
-  return m;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  return m;
-}
-
-// True when q = fl32(x * rcp) is known to encode to the same FP8 code as
-// fl32(x / scale) (see cast8).
-template <int FMT>
-__device__ __forceinline__ bool quotient_settled(float x, float q) {
-  constexpr uint32_t kMinNormal = (FMT == FMT_E4M3) ? 0x3C800000u : 0x38800000u;  // 2^-6, 2^-14
-  constexpr uint32_t kLowMask = (FMT == FMT_E4M3) ? 0xFFFFFu : 0x1FFFFFu;
-  constexpr uint32_t kMid = (FMT == FMT_E4M3) ? 0x80000u : 0x100000u;
-  const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
-  const uint32_t low = b & kLowMask;
-  const uint32_t dist = low > kMid ? low - kMid : kMid - low;
-  return (b >= kMinNormal && b < 0x7F800000u && dist > 8u) || x == 0.0f;
-}
-
-// 8 bf16 -> 8 FP8 bytes.  `scale` > 0, `rcp` = fl32(1 / scale): the codes of
-// fl32(x / scale) (IEEE binary32 division), clamped to +/-fmax and rounded to
-// nearest even by the hardware converter.
-//
-// The quotients are formed as q = fl32(x * rcp), which differs from x / scale
-// by at most 2^-23 relative, so fl32(x / scale) lies within a few binary32
-// steps of q.  An FP8 code only changes where the value crosses the midpoint
-// between two FP8 neighbours; in the FP8 normal range that midpoint has the
-// low 20 (e4m3) or 21 (e5m2) bits of the binary32 pattern equal to 0x80000 /
-// 0x100000.  When q's low bits are more than 8 steps from it, q and
-// fl32(x / scale) round to the same code (at binade edges the low bits are
-// near 0 or all ones, far from the midpoint).  Zero divides to a signed zero
-// (taken as is: rcp is infinite when scale is below 2^-128).  An element the
-// test cannot settle -- near a midpoint, in the FP8 subnormal
-// range, or not finite -- takes the IEEE division (one branch per 8 elements).
-template <int FMT>
-__device__ __forceinline__ uint2 cast8(uint4 c, float scale, float rcp) {
-  constexpr float fmax = Fp8<FMT>::fmax;
-  uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float x[8], t[8];
-  bool settled = true;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // a zero keeps its sign (x * rcp would give NaN when rcp is infinite)
-    t[i] = x[i] == 0.0f ? x[i] : x[i] * rcp;
-    settled = settled && quotient_settled<FMT>(x[i], t[i]);
-  }
-  if (__builtin_expect(!settled, 0)) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (!quotient_settled<FMT>(x[i], t[i])) t[i] = x[i] / scale;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(t[i], -fmax), fmax);
-  int lo = cvt_pk_fp8<FMT, false>(t[0], t[1], 0);
-  lo = cvt_pk_fp8<FMT, true>(t[2], t[3], lo);
-  int hi = cvt_pk_fp8<FMT, false>(t[4], t[5], 0);
-  hi = cvt_pk_fp8<FMT, true>(t[6], t[7], hi);
-  return make_uint2((uint32_t)lo, (uint32_t)hi);
-}
-
-// All-zero row: keep each zero's sign (0x00 / 0x80).
-__device__ __forceinline__ uint2 zero8(uint4 c) {
-  uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  uint32_t b[2] = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t s0 = (w[i] >> 15) & 1u, s1 = (w[i] >> 31) & 1u;
-    b[i / 2] |= ((s0 << 7) | (s1 << 15)) << (16 * (i % 2));
-  }
-  return make_uint2(b[0], b[1]);
-}
 
 template <int FMT, int R>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -175,9 +88,62 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
   }
 }
 
+// Few rows (decode): one workgroup of 256 threads per row, so a row's casts
+// spread over four SIMDs instead of one wavefront (a lone row of 4096 elements
+// is otherwise ~1300 dependent ALU instructions on one SIMD).  CPT chunks of
+// 8 elements per thread, all loads in flight at once; the amax is reduced
+// across the four wavefronts through LDS.
+constexpr int kRowThreads = 256;
+
+template <int FMT, int CPT>
+__global__ __launch_bounds__(kRowThreads) void quantize_row_per_block_kernel(const uint16_t* __restrict__ x,
+                                                                             int64_t cols, uint8_t* __restrict__ q,
+                                                                             float* __restrict__ scale) {
+  __shared__ uint32_t red[kRowThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nchunks = (int)(cols >> 3);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+  uint4 buf[CPT];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + kRowThreads * i;
+    buf[i] = c < nchunks ? xr[c] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) m = mag_max8(buf[i], m);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float amax = bf16_to_f32(m);
+  const float s = amax / Fp8<FMT>::fmax;
+  const float r = 1.0f / s;
+  if (tid == 0) scale[row] = (m == 0) ? 0.0f : s;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + kRowThreads * i;
+    if (c < nchunks) qr[c] = m == 0 ? zero8(buf[i]) : cast8<FMT>(buf[i], s, r);
+  }
+}
+
 template <int FMT>
 hipError_t launch_fmt(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                       hipStream_t stream) {
+  if (rows <= 64 && cols <= 16384) {
+    const int cpt = (int)(((cols >> 3) + kRowThreads - 1) / kRowThreads);
+#define SFR_QB(C)                                                                                          \
+  hipLaunchKernelGGL((quantize_row_per_block_kernel<FMT, C>), dim3((unsigned)rows), dim3(kRowThreads), 0, \
+                     stream, x, cols, q, scale)
+    if (cpt <= 1) SFR_QB(1);
+    else if (cpt <= 2) SFR_QB(2);
+    else if (cpt <= 4) SFR_QB(4);
+    else SFR_QB(8);
+#undef SFR_QB
+    return hipGetLastError();
+  }
   const int64_t per_lane = ((cols >> 3) + 63) / 64;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
 #define SFR_Q(R) hipLaunchKernelGGL((quantize_rows_kernel<FMT, R>), grid, block, 0, stream, x, rows, cols, q, scale)

@@ -33,4 +33,9 @@ struct LinearArgs {
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
+// Row-wise quantization of x into (xq, xs) and the linear layer on them (a's
+// xq / xs are ignored): one fused launch for small decode shapes, else two.
+hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a,
+                                 hipStream_t stream);
+
 }  // namespace sfr

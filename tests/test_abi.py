@@ -29,7 +29,7 @@ def test_header_declares_the_api():
     names = declared_functions()
     for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
               "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
-              "sparse_fp8_scaled_linear"):
+              "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic"):
         assert n in names
 
 
@@ -138,6 +138,26 @@ def test_scaled_linear_validation(lib):
     assert call(m=0, xq=None, xs=None, out=None) == OK
     assert call(xs=None) == NULL
     assert call(ws=U) == ALIGN
+
+
+def test_dynamic_linear_validation(lib):
+    f = lib.sparse_fp8_rowwise_linear_dynamic
+    good = dict(x=A, xd=0, m=4, k=1024, v=A, meta=A, wd=1, ws=A, wk=0, n=32, bias=None, out=A, od=0, xq=A, xs=A)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["x"], a["xd"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["wk"], a["n"], a["bias"],
+                 a["out"], a["od"], a["xq"], a["xs"], None)
+
+    assert call(xd=7) == DTYPE
+    assert call(wk=3) == DTYPE
+    assert call(k=1000) == SHAPE
+    assert call(n=40) == SHAPE
+    assert call(m=0, x=None, xq=None, xs=None, out=None) == OK
+    assert call(xq=None) == NULL
+    assert call(xs=None) == NULL
+    assert call(xs=U) == ALIGN
+    assert call(x=U) == ALIGN
 
 
 def test_binding_rejects_host_tensors():
