@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GB/s measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-algo-search", action="store_true", help="skip the per-shape kernel configuration search")
     p.add_argument("--cpu-rows", type=int, default=160, help="activation rows in the CPU oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (for scaling HBM byte counters) and exit")
@@ -228,6 +229,9 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(torch, sfr, sfr_inputs, lib, dev, stream)
 
+    if not args.no_algo_search:
+        result["algo_search"] = bench_algo_search()
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
     print(json.dumps(result), flush=True)
@@ -275,6 +279,24 @@ def bench_tensorwise(torch, sfr, lib, w, x, M, N, K, h, stream, steps=20, warmup
             "TFLOP/s": round(2.0 * M * N * K / (step_ms * 1e-3) / 1e12, 2),
             "kernels_ms": {"quantize_tensorwise": round(q_ms, 5), "gemm": round(g_ms, 5)},
             "quantize_gbs": round(quant_bytes(M, K) / (q_ms * 1e-3) / 1e9, 1)}
+
+
+def bench_algo_search():
+    """Per-shape kernel configuration search (sparse_fp8_row_amd.tune) over the
+    Llama-3.1-8B layer shapes at M in {16, 512, 8192}, e4m3 x e4m3: the
+    built-in choice against the fastest configuration."""
+    from sparse_fp8_row_amd import tune
+    import sfr_inputs
+    shapes = [(m, n, k) for (n, k) in sfr_inputs.LLAMA_SHAPES.values() for m in (16, 512, 8192)]
+    res = tune.search(shapes, reps=10, warmup=2)
+    out = {}
+    for r in res["timings"]:
+        key = f"M{r['m']}N{r['n']}K{r['k']}"
+        out[key] = {"default": r["default"], "default_us": r["default_us"], "best": r["best"], "best_us": r["best_us"],
+                    "us": r["us"]}
+        print(f"[bench] algo {key}: default {r['default']} {r['default_us']} us, best {r['best']} {r['best_us']} us",
+              file=sys.stderr, flush=True)
+    return out
 
 
 def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):

@@ -230,6 +230,42 @@ sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, 
                                              const uint16_t* bias, void* out, sfr_out_t out_dt,
                                              uint8_t* xq, float* xs, void* stream);
 
+/*
+ * Kernel configurations ("algorithms") of the linear layer, and the choice
+ * among them.  Source: pytorch/ao PR #4432 ("Add algorithm search to FP8
+ * sparse linear benchmark": the best kernel configuration depends on the
+ * shape, so it is searched per shape) and PR #1671 (remaining tasks: a
+ * meaningful config selection).  Every algorithm computes the same function
+ * (same result rules; the order of the binary32 sum differs between them).
+ *
+ *   sfr_linear_algo_count()      number of algorithms (ids 0 .. count-1).
+ *   sfr_linear_algo_name(a)      static name, NULL for an unknown id.
+ *   sfr_linear_algo_supported(a, m, n, k)
+ *                                1 if algorithm a can run the shape, else 0.
+ *   sfr_linear_default_algo(m, n, k)
+ *                                the library's built-in choice for the shape.
+ *   sparse_fp8_scaled_linear_algo(..., algo, stream)
+ *                                sparse_fp8_scaled_linear with the given
+ *                                algorithm; SFR_ALGO_DEFAULT (-1) = built-in
+ *                                choice.  An id out of range is
+ *                                SFR_ERR_DTYPE; an algorithm that cannot run
+ *                                the shape is SFR_ERR_SHAPE.
+ * Ids: 0 decode_lds (m <= 16, k % 1024 == 0, k <= 16384), 1 decode_reg
+ * (m <= 16), 2 tiled_64x64, 3 tiled_128x128, 4 tiled_256x256, 5 wide_256x256
+ * (k >= 512).
+ */
+#define SFR_ALGO_DEFAULT (-1)
+int sfr_linear_algo_count(void);
+const char* sfr_linear_algo_name(int algo);
+int sfr_linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k);
+int sfr_linear_default_algo(int64_t m, int64_t n, int64_t k);
+sfr_status sparse_fp8_scaled_linear_algo(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs,
+                                         sfr_scale_t xs_kind, int64_t m, int64_t k,
+                                         const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                         const float* ws, sfr_scale_t ws_kind, int64_t n,
+                                         const uint16_t* bias, void* out, sfr_out_t out_dt, int algo,
+                                         void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sfr_status_string(sfr_status s);
 

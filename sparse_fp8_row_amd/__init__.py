@@ -36,7 +36,8 @@ STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN"
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
 EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
             "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
-            "sparse_fp8_rowwise_linear_dynamic",
+            "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count",
+            "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
             "sfr_status_string", "sfr_format_version")
 
 _FP8 = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
@@ -64,6 +65,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
     lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
     lib.sparse_fp8_rowwise_linear_dynamic.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, P]
+    lib.sparse_fp8_scaled_linear_algo.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, I, P]
+    lib.sparse_fp8_scaled_linear_algo.restype = I
+    lib.sfr_linear_algo_count.argtypes = []
+    lib.sfr_linear_algo_count.restype = I
+    lib.sfr_linear_algo_name.argtypes = [I]
+    lib.sfr_linear_algo_name.restype = ctypes.c_char_p
+    lib.sfr_linear_algo_supported.argtypes = [I, I64, I64, I64]
+    lib.sfr_linear_algo_supported.restype = I
+    lib.sfr_linear_default_algo.argtypes = [I64, I64, I64]
+    lib.sfr_linear_default_algo.restype = I
     for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
                lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic):
         fn.restype = I
@@ -141,13 +152,57 @@ def compress_2to4_fp8(wq: torch.Tensor, stream=None):
     return values, meta
 
 
+SFR_ALGO_DEFAULT = -1
+# Algorithm table consulted by sparse_fp8_scaled_linear when no algo is given:
+# {(m_bucket, n, k): algo}, filled by set_algo_table (see tune.py).
+_algo_table = {}
+M_BUCKETS = (1, 4, 16, 64, 256, 1024, 4096, 1 << 62)
+
+
+def m_bucket(m: int) -> int:
+    """Upper bound of m's bucket: rows 1, 2-4, 5-16, 17-64, ... share a table entry."""
+    for b in M_BUCKETS:
+        if m <= b:
+            return b
+    return M_BUCKETS[-1]
+
+
+def linear_algos():
+    """[(id, name)] of the linear layer's kernel configurations."""
+    lib = load()
+    return [(i, lib.sfr_linear_algo_name(i).decode()) for i in range(lib.sfr_linear_algo_count())]
+
+
+def algo_supported(algo: int, m: int, n: int, k: int) -> bool:
+    return bool(load().sfr_linear_algo_supported(algo, m, n, k))
+
+
+def default_algo(m: int, n: int, k: int) -> int:
+    return int(load().sfr_linear_default_algo(m, n, k))
+
+
+def set_algo_table(table: dict):
+    """Use {(m_bucket, n, k): algo} (e.g. from tune.search) for later calls; an
+    entry whose algorithm cannot run a shape is ignored for that shape."""
+    _algo_table.clear()
+    _algo_table.update({(int(b), int(n), int(k)): int(a) for (b, n, k), a in table.items()})
+
+
+def _table_algo(m: int, n: int, k: int) -> int:
+    a = _algo_table.get((m_bucket(m), n, k), SFR_ALGO_DEFAULT)
+    return a if a == SFR_ALGO_DEFAULT or algo_supported(a, m, n, k) else SFR_ALGO_DEFAULT
+
+
 def sparse_fp8_scaled_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.Tensor, meta: torch.Tensor,
                              ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                             out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+                             out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None,
+                             algo: Optional[int] = None):
     """out[m, n] = xs * ws * sum_k xq[m, k] * wq[n, k] (+ bias[n]), as bf16 (or float32).
 
     Each scale is per row (xs [m], ws [n]) or one for the tensor (shape [1]);
-    the granularity follows from the scale's length."""
+    the granularity follows from the scale's length.  `algo` picks the kernel
+    configuration (see linear_algos); None uses the table set by
+    set_algo_table, else the library's built-in choice."""
     for t, nm in ((xq, "xq"), (xs, "xs"), (values, "values"), (meta, "meta"), (ws, "ws")):
         _dev(t, nm)
     m, k = xq.shape
@@ -169,10 +224,12 @@ def sparse_fp8_scaled_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.T
         out = torch.empty((m, n), dtype=out_dtype, device=xq.device)
     elif out.shape != (m, n) or out.dtype != out_dtype or not out.is_contiguous():
         raise ValueError("out has the wrong shape or dtype")
-    _check(load().sparse_fp8_scaled_linear(
+    if algo is None:
+        algo = _table_algo(m, n, k)
+    _check(load().sparse_fp8_scaled_linear_algo(
         xq.data_ptr(), _fp8_enum(xq.dtype), xs.data_ptr(), xk, m, k, values.data_ptr(), meta.data_ptr(),
         _fp8_enum(values.dtype), ws.data_ptr(), wk, n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od,
-        _stream(stream)), "sparse_fp8_scaled_linear")
+        int(algo), _stream(stream)), "sparse_fp8_scaled_linear")
     return out
 
 

@@ -1031,66 +1031,105 @@ hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const Lin
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel configurations ("algorithms") and the default choice by shape
+// ---------------------------------------------------------------------------
 template <int XF, int WF, int OUT>
-hipError_t run_linear(const LinearArgs& a, hipStream_t stream) {
-  if (a.m <= 16) {
-    // LDS-staged decode when the 16-row weight block (10 K bytes) fits in LDS,
-    // with the activation staged too when it also fits
-    constexpr int64_t kLds = 160 * 1024;
-    if (a.k % 1024 == 0 && 10 * a.k <= kLds) {
-      const bool xl = 10 * a.k + a.m * a.k <= kLds;
-      const unsigned lds = (unsigned)(10 * a.k + (xl ? a.m * a.k : 0));
-      auto kern = xl ? linear_decode_lds_kernel<XF, WF, OUT, true> : linear_decode_lds_kernel<XF, WF, OUT, false>;
-      static bool attr_set[2] = {false, false};  // benign race: every thread sets the same value
-      if (!attr_set[xl]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-        if (e != hipSuccess) return e;
-        attr_set[xl] = true;
-      }
-      hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(256), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                         a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
-      return hipGetLastError();
-    }
-    const int64_t kt = a.k / KSTEP;
-    const dim3 grid((unsigned)(a.n / 16));
+hipError_t run_decode_lds(const LinearArgs& a, hipStream_t stream) {
+  // the activation is staged in LDS too when it fits beside the weight block
+  constexpr int64_t kLds = 160 * 1024;
+  const bool xl = 10 * a.k + a.m * a.k <= kLds;
+  const unsigned lds = (unsigned)(10 * a.k + (xl ? a.m * a.k : 0));
+  auto kern = xl ? linear_decode_lds_kernel<XF, WF, OUT, true> : linear_decode_lds_kernel<XF, WF, OUT, false>;
+  static bool attr_set[2] = {false, false};  // benign race: every thread sets the same value
+  if (!attr_set[xl]) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (e != hipSuccess) return e;
+    attr_set[xl] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(256), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
+  return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT>
+hipError_t run_decode_reg(const LinearArgs& a, hipStream_t stream) {
+  const int64_t kt = a.k / KSTEP;
+  const dim3 grid((unsigned)(a.n / 16));
 #define SFR_DEC(NWV, U)                                                                                      \
   hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT, NWV, U>), grid, dim3(64 * NWV), 0, stream, a.xq, a.xs, \
                      a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride)
-    if (kt <= 8) SFR_DEC(8, 1);
-    else if (kt <= 16) SFR_DEC(8, 2);
-    else if (kt <= 32) SFR_DEC(8, 4);
-    else if (kt <= 64) SFR_DEC(16, 4);
-    else if (kt <= 112) SFR_DEC(16, 7);
-    else SFR_DEC(16, 8);  // loops for kt > 128
+  if (kt <= 8) SFR_DEC(8, 1);
+  else if (kt <= 16) SFR_DEC(8, 2);
+  else if (kt <= 32) SFR_DEC(8, 4);
+  else if (kt <= 64) SFR_DEC(16, 4);
+  else if (kt <= 112) SFR_DEC(16, 7);
+  else SFR_DEC(16, 8);  // loops for kt > 128
 #undef SFR_DEC
-    return hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT>
+hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
+  switch (algo) {
+    case ALGO_DECODE_LDS: return run_decode_lds<XF, WF, OUT>(a, stream);
+    case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
+    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
+    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
+    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
+    default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
   }
-  const int64_t big = ((a.m + 255) / 256) * ((a.n + 255) / 256);
-  const int64_t mid = ((a.m + 127) / 128) * ((a.n + 127) / 128);
-  if (big >= 512) {
-    if (a.k >= 4 * KSTEP) return run_wide<XF, WF, OUT, 8>(a, stream);
-    return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
-  }
-  if (mid >= 256) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
-  return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
 }
 
 template <int XF, int WF>
-hipError_t run_out(const LinearArgs& a, hipStream_t stream) {
-  if (a.out_fmt == OUT_BF16) return run_linear<XF, WF, OUT_BF16>(a, stream);
-  return run_linear<XF, WF, OUT_F32>(a, stream);
+hipError_t run_out(const LinearArgs& a, int algo, hipStream_t stream) {
+  if (a.out_fmt == OUT_BF16) return run_algo<XF, WF, OUT_BF16>(a, algo, stream);
+  return run_algo<XF, WF, OUT_F32>(a, algo, stream);
 }
 
 }  // namespace
 
-hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_out<FMT_E4M3, FMT_E4M3>(a, stream);
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_out<FMT_E4M3, FMT_E5M2>(a, stream);
-  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_out<FMT_E5M2, FMT_E4M3>(a, stream);
-  return run_out<FMT_E5M2, FMT_E5M2>(a, stream);
+const char* linear_algo_name(int algo) {
+  static const char* const names[ALGO_COUNT] = {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128",
+                                                "tiled_256x256", "wide_256x256"};
+  return algo >= 0 && algo < ALGO_COUNT ? names[algo] : nullptr;
 }
 
+bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  switch (algo) {
+    case ALGO_DECODE_LDS: return m <= 16 && k % 1024 == 0 && 10 * k <= 160 * 1024;
+    case ALGO_DECODE_REG: return m <= 16;
+    case ALGO_TILED_64:
+    case ALGO_TILED_128:
+    case ALGO_TILED_256: return true;
+    case ALGO_WIDE_256: return k >= 4 * KSTEP;
+    default: return false;
+  }
+}
+
+// The built-in choice: decode kernels up to 16 rows (LDS-staged when the
+// weight block fits), then the largest tile that still gives at least 256
+// (128, 64) or 512 (256) tiles, the pipelined kernel for 256 x 256 when K allows.
+int linear_default_algo(int64_t m, int64_t n, int64_t k) {
+  if (m <= 16) return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
+  const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t mid = ((m + 127) / 128) * ((n + 127) / 128);
+  if (big >= 512) return k >= 4 * KSTEP ? ALGO_WIDE_256 : ALGO_TILED_256;
+  if (mid >= 256) return ALGO_TILED_128;
+  return ALGO_TILED_64;
+}
+
+hipError_t launch_linear_algo(const LinearArgs& a, int algo, hipStream_t stream) {
+  if (algo < 0) algo = linear_default_algo(a.m, a.n, a.k);
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_out<FMT_E4M3, FMT_E4M3>(a, algo, stream);
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_out<FMT_E4M3, FMT_E5M2>(a, algo, stream);
+  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_out<FMT_E5M2, FMT_E4M3>(a, algo, stream);
+  return run_out<FMT_E5M2, FMT_E5M2>(a, algo, stream);
+}
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) { return launch_linear_algo(a, -1, stream); }
 
 template <int XF, int WF>
 hipError_t run_fused_out(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {

@@ -33,6 +33,21 @@ struct LinearArgs {
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
+// Kernel configurations of the linear layer.  algo < 0: the built-in choice.
+enum LinearAlgo {
+  ALGO_DECODE_LDS = 0,  // m <= 16: 16 weight rows per workgroup, staged in LDS
+  ALGO_DECODE_REG = 1,  // m <= 16: 16 weight rows per workgroup, streamed to registers
+  ALGO_TILED_64 = 2,    // 64 x 64 tiles, 4 wavefronts
+  ALGO_TILED_128 = 3,   // 128 x 128 tiles, 4 wavefronts
+  ALGO_TILED_256 = 4,   // 256 x 256 tiles, 8 wavefronts
+  ALGO_WIDE_256 = 5,    // 256 x 256 tiles, 4 software-pipelined wavefronts (k >= 512)
+  ALGO_COUNT = 6
+};
+const char* linear_algo_name(int algo);
+bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k);
+int linear_default_algo(int64_t m, int64_t n, int64_t k);
+hipError_t launch_linear_algo(const LinearArgs& a, int algo, hipStream_t stream);
+
 // Row-wise quantization of x into (xq, xs) and the linear layer on them (a's
 // xq / xs are ignored): one fused launch for small decode shapes, else two.
 hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a,

@@ -29,7 +29,8 @@ def test_header_declares_the_api():
     names = declared_functions()
     for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
               "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
-              "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic"):
+              "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo",
+              "sfr_linear_algo_count", "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo"):
         assert n in names
 
 
@@ -158,6 +159,48 @@ def test_dynamic_linear_validation(lib):
     assert call(xs=None) == NULL
     assert call(xs=U) == ALIGN
     assert call(x=U) == ALIGN
+
+
+def test_linear_algos(lib):
+    names = [lib.sfr_linear_algo_name(i) for i in range(lib.sfr_linear_algo_count())]
+    assert names == [b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128", b"tiled_256x256",
+                     b"wide_256x256"]
+    assert lib.sfr_linear_algo_name(6) is None and lib.sfr_linear_algo_name(-1) is None
+    sup = lambda a, m, n, k: lib.sfr_linear_algo_supported(a, m, n, k)
+    assert sup(0, 16, 4096, 4096) == 1 and sup(0, 17, 4096, 4096) == 0      # decode: m <= 16
+    assert sup(0, 4, 4096, 640) == 0                                        # LDS decode: k % 1024
+    assert sup(0, 4, 4096, 16384) == 1 and sup(0, 4, 4096, 17408) == 0      # weight block must fit LDS
+    assert sup(1, 16, 4096, 640) == 1 and sup(1, 17, 4096, 640) == 0
+    assert all(sup(a, 5000, 4096, 256) == 1 for a in (2, 3, 4))
+    assert sup(5, 5000, 4096, 384) == 0 and sup(5, 5000, 4096, 512) == 1   # pipelined: k >= 512
+    assert sup(2, 4, 100, 256) == 0 and sup(6, 4, 128, 256) == 0           # bad n, unknown id
+    # the built-in choice
+    d = lib.sfr_linear_default_algo
+    assert d(1, 4096, 4096) == 0 and d(16, 4096, 14336) == 0 and d(16, 4096, 17408) == 1
+    assert d(8192, 14336, 4096) == 5 and d(8192, 14336, 256) == 4
+    assert d(512, 14336, 4096) == 3 and d(512, 4096, 4096) == 2
+
+
+def test_linear_algo_validation(lib):
+    f = lib.sparse_fp8_scaled_linear_algo
+    good = dict(xq=A, xd=0, xs=A, xk=0, m=4, k=256, v=A, meta=A, wd=0, ws=A, wk=0, n=32, bias=None, out=A, od=0,
+                algo=-1)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["xq"], a["xd"], a["xs"], a["xk"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["wk"],
+                 a["n"], a["bias"], a["out"], a["od"], a["algo"], None)
+
+    assert call(algo=6) == DTYPE and call(algo=-2) == DTYPE
+    assert call(algo=0) == SHAPE                  # k = 256: not a multiple of 1024
+    assert call(algo=5) == SHAPE                  # k < 512
+    assert call(algo=1, xq=None) == NULL          # supported: validation goes on
+    assert call(algo=2, m=0, xq=None, xs=None, out=None) == OK
+
+
+def test_algo_table_buckets():
+    import sparse_fp8_row_amd as sfr
+    assert [sfr.m_bucket(m) for m in (1, 2, 4, 5, 16, 17, 8192, 9000)] == [1, 4, 4, 16, 16, 64, 1 << 62, 1 << 62]
 
 
 def test_binding_rejects_host_tensors():

@@ -1,0 +1,91 @@
+"""GPU parity of every kernel configuration of the linear layer
+(sparse_fp8_scaled_linear_algo) against the oracle, on shapes each one
+supports -- a decode shape every algorithm can run, a tall shape for the tiled
+ones and the decode kernel's largest K -- plus the per-shape search
+(sparse_fp8_row_amd.tune) and the table it feeds."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sfr_inputs
+from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_f32, hw_bound, FP8_TORCH
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = oracle.E4M3, oracle.E5M2
+SHAPES = [("all_algos", 7, 1040, 1024, E4, E4, True), ("tiled", 300, 4112, 640, E5, E4, True),
+          ("max_k_decode", 16, 256, 16384, E4, E5, False)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_fp8_row_amd as sfr
+    sfr.load()
+    return sfr
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s[0])
+def test_every_algo(gpu, shape):
+    name, m, n, k, xf, wf, has_bias = shape
+    case = sfr_inputs.Case(f"algo_{name}", 13, m, n, k, x_fmt=xf, w_fmt=wf, bias=has_bias)
+    xb, wb, bb = sfr_inputs.draw_x(case), sfr_inputs.draw_w(case), sfr_inputs.draw_bias(case)
+    oxq, oxs = oracle.quantize_rows(xb, xf)
+    owq, ows = oracle.quantize_rows(wb, wf)
+    ov, om = oracle.compress_2to4(owq)
+    ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows, bias=bb)
+    hwb = hw_bound(oxq, xf, oxs, oracle.decompress_2to4(ov, om), wf, ows, np.arange(m), np.arange(n))
+    xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(xb), FP8_TORCH[xf])
+    pw = gpu.prepare_weight(dev_bf16(wb), FP8_TORCH[wf])
+    b = None if bb is None else dev_bf16(bb)
+    ran = []
+    for algo, aname in gpu.linear_algos():
+        if not gpu.algo_supported(algo, m, n, k):
+            with pytest.raises(gpu.SfrError):
+                gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, b, algo=algo)
+            continue
+        for od in (torch.bfloat16, torch.float32):
+            say(f"algo {aname} {case.name} out={od}")
+            y = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, b, out_dtype=od, algo=algo)
+            torch.cuda.synchronize()
+            if od == torch.float32:
+                r = check_f32(host_f32(y), ref, bb is not None, hwb)
+            else:
+                r = check_bf16(host_bf16_bits(y), ref, hwb)
+            say(f"  {r}")
+            assert r["bad"] == 0, r
+            assert r["strict_rate_ok"], r
+        ran.append(aname)
+    assert len(ran) >= 4
+
+
+def test_search_and_table(gpu):
+    from sparse_fp8_row_amd import tune
+    shapes = [(16, 1024, 1024), (300, 1024, 640)]
+    res = tune.search(shapes, reps=3, warmup=1)
+    names = dict(gpu.linear_algos())
+    for (m, n, k), rec in zip(shapes, res["timings"]):
+        best = res["table"][(gpu.m_bucket(m), n, k)]
+        assert gpu.algo_supported(best, m, n, k)
+        assert names[best] == rec["best"] and rec["best_us"] == min(rec["us"].values())
+    # the table drives later calls: same bytes as the explicit algorithm
+    case = sfr_inputs.Case("algo_table", 14, 300, 1024, 640, bias=True)
+    xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(sfr_inputs.draw_x(case)))
+    pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)))
+    best = res["table"][(gpu.m_bucket(300), 1024, 640)]
+    gpu.set_algo_table(res["table"])
+    try:
+        y1 = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale)
+    finally:
+        gpu.set_algo_table({})
+    y2 = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, algo=best)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(y1), host_bf16_bits(y2))
