@@ -62,7 +62,10 @@ def parse():
 # them changes, the stored figure no longer describes the kernel and is not reported.
 TRAFFIC_SOURCES = ("sparse_fp8_row_amd/csrc/gemm.hip", "sparse_fp8_row_amd/csrc/sfr_device.hpp",
                    "sparse_fp8_row_amd/csrc/sfr_launch.hpp")
-TRAFFIC_FILE = "profiles/traffic_linear_wide_prefill_up.txt"
+TRAFFIC_FILE = "profiles/traffic_linear_prefill_up.txt"
+# the kernel behind each configuration the prefill workload can take
+ALGO_KERNELS = {2: "linear_tiled_kernel (64x64 tile, 4 wavefronts)", 3: "linear_tiled_kernel (128x128 tile, 4 wavefronts)",
+                4: "linear_tiled_kernel (256x256 tile, 8 wavefronts)", 5: "linear_wide_kernel (256x256 tile, 4 wavefronts)"}
 COPY_BYTES = 1 << 30
 
 
@@ -213,7 +216,7 @@ def main():
                                "e4m3 x e4m3, bf16 out, no bias",
                    "m": M, "n": N, "k": K, "x_dtype": "e4m3", "w_dtype": "e4m3", "out_dtype": "bf16",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "linear_wide_kernel (256x256 tile, 4 wavefronts)",
+        "roofline": {"bound": "mfma", "kernel": ALGO_KERNELS.get(sfr.default_algo(M, N, K), "?"),
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "frac_of_sparse_peak": round(gemm_tflops / PEAK_FP8_SPARSE_TFLOPS, 4),
@@ -300,7 +303,9 @@ def bench_algo_search():
 
 
 def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
-    """GEMM GB/s at M in {1,4,16}, K=N=4096, bf16 bias, rotating weights (> 512 MB)."""
+    """GEMM GB/s at M in {1,4,16}, K=N=4096, bf16 bias, rotating weights (> 512 MB);
+    per-call times from a HIP graph of the calls (the eager loop's rate too)."""
+    from sparse_fp8_row_amd import tune
     res = {}
     n, k = 4096, 4096
     case0 = sfr_inputs.decode_cases()[0]
@@ -321,11 +326,11 @@ def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
         xq, xs = sfr.quantize_rowwise_fp8(x, torch.float8_e4m3fn)
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
 
-        def call(i):
+        def call(i, hs=h):
             st = lib.sparse_fp8_rowwise_linear(xq.data_ptr(), sfr.SFR_E4M3, xs.data_ptr(), m, k,
                                                vals[i].data_ptr(), metas[i].data_ptr(), sfr.SFR_E4M3,
                                                base.scale.data_ptr(), n, bias.data_ptr(), out.data_ptr(),
-                                               sfr.SFR_OUT_BF16, h)
+                                               sfr.SFR_OUT_BF16, hs)
             assert st == 0, st
 
         for i in range(copies):
@@ -338,46 +343,42 @@ def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
             call(i % copies)
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        eager_us = e0.elapsed_time(e1) * 1e3 / reps
+        # the same calls replayed from a HIP graph: the GPU's own rate (an
+        # eager loop of few-microsecond launches is paced by the host)
+        us = tune.graph_us(call, copies, calls=2 * copies)
         b = gemm_bytes(m, n, k, True)
         gbs = b / (us * 1e-6) / 1e9
         res[f"M{m}"] = {"us_per_call": round(us, 3), "bytes": b, "GB/s": round(gbs, 1),
-                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
-        print(f"[bench] decode M={m}: {us:.3f} us/call, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "eager_us_per_call": round(eager_us, 3)}
+        print(f"[bench] decode M={m}: {us:.3f} us/call in a graph ({eager_us:.3f} eager), {gbs:.1f} GB/s",
+              file=sys.stderr, flush=True)
 
         # the layer from the bf16 activation: quantization + GEMM as two
         # launches, and fused into one (sparse_fp8_rowwise_linear_dynamic)
         xq2 = torch.empty_like(xq)
         xs2 = torch.empty_like(xs)
 
-        def two(i):
-            st = lib.quantize_rowwise_fp8(x.data_ptr(), m, k, sfr.SFR_E4M3, xq2.data_ptr(), xs2.data_ptr(), h)
+        def two(i, hs=h):
+            st = lib.quantize_rowwise_fp8(x.data_ptr(), m, k, sfr.SFR_E4M3, xq2.data_ptr(), xs2.data_ptr(), hs)
             assert st == 0, st
             st = lib.sparse_fp8_rowwise_linear(xq2.data_ptr(), sfr.SFR_E4M3, xs2.data_ptr(), m, k,
                                                vals[i].data_ptr(), metas[i].data_ptr(), sfr.SFR_E4M3,
                                                base.scale.data_ptr(), n, bias.data_ptr(), out.data_ptr(),
-                                               sfr.SFR_OUT_BF16, h)
+                                               sfr.SFR_OUT_BF16, hs)
             assert st == 0, st
 
-        def fused(i):
+        def fused(i, hs=h):
             st = lib.sparse_fp8_rowwise_linear_dynamic(x.data_ptr(), sfr.SFR_E4M3, m, k, vals[i].data_ptr(),
                                                        metas[i].data_ptr(), sfr.SFR_E4M3, base.scale.data_ptr(),
                                                        sfr.SFR_SCALE_ROW, n, bias.data_ptr(), out.data_ptr(),
-                                                       sfr.SFR_OUT_BF16, xq2.data_ptr(), xs2.data_ptr(), h)
+                                                       sfr.SFR_OUT_BF16, xq2.data_ptr(), xs2.data_ptr(), hs)
             assert st == 0, st
 
         for name, fn in (("quantize_plus_gemm", two), ("fused", fused)):
-            for i in range(copies):
-                fn(i)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for i in range(reps):
-                fn(i % copies)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e3 / reps
+            t = tune.graph_us(fn, copies, calls=2 * copies)
             res[f"M{m}"][f"{name}_us_per_call"] = round(t, 3)
-            print(f"[bench] decode M={m} from bf16, {name}: {t:.3f} us/call", file=sys.stderr, flush=True)
+            print(f"[bench] decode M={m} from bf16, {name}: {t:.3f} us/call in a graph", file=sys.stderr, flush=True)
     return res
 
 

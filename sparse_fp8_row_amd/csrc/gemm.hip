@@ -39,6 +39,7 @@
 //    Tokens beyond M are zero columns of B, the padding-to-16 idea of
 //    pytorch/ao PR #1734 ("promote blocksparse from prototype ...").
 #include <type_traits>
+#include <utility>
 
 #include "sfr_device.hpp"
 #include "sfr_launch.hpp"
@@ -654,183 +655,172 @@ __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
   }
 }
 
-// Decode kernel, LDS-staged variant.  A workgroup of 4 wavefronts owns 16
-// weight rows.  Their compressed values (16 x K/2 bytes) and metadata
-// (16 x K/8 bytes) are one contiguous block each in memory, so they are read
-// with 1 KB contiguous global_load_lds instructions into LDS, then each
-// wavefront runs the MFMAs of a quarter of the k steps from there.  Chunks are
-// XOR-swizzled within their 128-byte group by (row & 7) on the way in (a
-// permutation inside each 1 KB load, so reads stay contiguous), which makes the
-// MFMA-layout reads conflict-free.  The activation is read directly.
-template <int XF, int WF, int OUT, bool XL>
-__global__ __launch_bounds__(256) void linear_decode_lds_kernel(
+// b[s] = lanes 2s (low half) and 2s + 1 (high half) of each 16-lane row of x,
+// broadcast to the row (DPP row_newbcast, control 0x150 + lane)
+template <int S>
+__device__ __forceinline__ v8i row_bcast_pair(const v4i& x) {
+  v8i r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    r[d] = __builtin_amdgcn_update_dpp(0, x[d], 0x150 + 2 * S, 0xF, 0xF, false);
+    r[4 + d] = __builtin_amdgcn_update_dpp(0, x[d], 0x151 + 2 * S, 0xF, 0xF, false);
+  }
+  return r;
+}
+template <int... S>
+__device__ __forceinline__ void row_bcast_steps(v8i (&b)[8], const v4i& x, std::integer_sequence<int, S...>) {
+  ((b[S] = row_bcast_pair<S>(x)), ...);
+}
+
+// Decode kernel, one k unit per wavefront.  A workgroup owns RT * 16 weight
+// rows and K / 1024 "units" of 1024 k (8 MFMA steps) each; wavefront w takes
+// units w, w + NW, ...  For a unit it puts the unit's compressed values
+// (512 contiguous bytes per row) and metadata (128 bytes per row) in flight
+// into its own RT * 10 KB of LDS with 1 KB global_load_lds instructions, and
+// the activation operands of the unit's 8 steps straight into registers
+// (shared by the RT row tiles), then waits for its own loads only and runs
+// the 8 * RT MFMAs: no workgroup barrier before the final fixed-order
+// reduction, so every wavefront computes as soon as its data is there while
+// the others' loads stream.  LDS holds only the weight block, so several
+// workgroups share a CU.  Each 16-byte chunk of a row is stored at
+// chunk ^ (row & 7) (a permutation inside 128-byte groups, applied to the
+// source addresses of each 1 KB load), which makes the MFMA-layout LDS reads
+// conflict-free.  RT = 2 halves the activation traffic (every workgroup reads
+// all of the activation) at half the workgroups.
+constexpr int kUnitK = 1024;
+constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
+template <int XF, int WF, int OUT, int RT, bool X1>
+__global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int xs_stride, int ws_stride) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NW = blockDim.x / 64;
   const int r16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int KT = K / KSTEP;
-  const int vbytes = 16 * (K / 2), mbytes = 16 * (K / 8);  // multiples of 1 KB (K % 128 == 0)
-  const uint8_t* vblk = values + (int64_t)n0 * (K / 2);
-  const uint8_t* mblk = meta + (int64_t)n0 * (K / 8);
-  const int vchunks_row = K / 32, mchunks_row = K / 128;   // 16-byte chunks per row
+  const int NU = K / kUnitK;
+  uint8_t* region = smem + wave * (RT * kUnitLds);
+  // DMA lane roles: values load i covers rows 2i, 2i + 1 of a row tile (32
+  // chunks each), at a uniform offset i * K plus a lane offset that repeats
+  // with period 4 in i (the swizzle depends on row & 7); metadata load i covers
+  // rows 8i .. 8i + 7 (8 chunks each), uniform offset i * K plus one lane offset
+  const int vrow_l = lane >> 5, vc = lane & 31, mrow_l = lane >> 3, mc = lane & 7;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(vrow_l * (K / 2) + 16 * (vc ^ ((2 * i + vrow_l) & 7)));
+  const uint32_t moff = (uint32_t)(mrow_l * (K / 8) + 16 * (mc ^ (mrow_l & 7)));
+  // rows m >= M read row M - 1: MFMA output column m depends on activation
+  // row m alone, and those columns are never stored
+  const uint8_t* xrow = xq + (int64_t)min(r16, M - 1) * K + 16 * lg;
+  // LDS read offsets: step s's values chunk 4s + lg of row r16 sits at chunk
+  // (4s + lg) ^ (r16 & 7) = 8 (s >> 1) + ab[s & 1]; its metadata chunk at s ^ (r16 & 7)
+  const int r7 = r16 & 7;
+  const uint32_t a_even = r16 * 512 + 16 * ((4 * ((r7 >> 2) & 1)) | (lg ^ (r7 & 3)));
+  const uint32_t a_odd = r16 * 512 + 16 * ((4 * (((r7 >> 2) & 1) ^ 1)) | (lg ^ (r7 & 3)));
+  const uint32_t i_row = 8192 + r16 * 128 + 4 * lg;
 
-  // epilogue operands up front
-  const int m = r16, n = n0 + 4 * lg;
+  const int m = r16;
   float xsm = 0.f;
-  v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
-  uint2 b2 = make_uint2(0, 0);
+  v4f w4[RT];
+  uint2 b2[RT];
   if (wave == 0) {
     xsm = xs[min(m, M - 1) * xs_stride];
-    w4 = load_ws4(ws, n, ws_stride);
-    if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int n = (blockIdx.x * RT + t) * 16 + 4 * lg;
+      w4[t] = load_ws4(ws, n, ws_stride);
+      b2[t] = bias ? *reinterpret_cast<const uint2*>(bias + n) : make_uint2(0, 0);
+    }
   }
-  // stream the block into LDS: LDS chunk p holds global chunk p ^ (row(p) & 7)
-  for (int q = wave; q < vbytes / 1024; q += 4) {
-    const int p = q * 64 + lane, row = p / vchunks_row;
-    __builtin_amdgcn_global_load_lds((void*)(vblk + 16 * (p ^ (row & 7))), (void*)(smem + q * 1024), 16, 0, 0);
-  }
-  for (int q = wave; q < mbytes / 1024; q += 4) {
-    const int p = q * 64 + lane, row = p / mchunks_row;
-    __builtin_amdgcn_global_load_lds((void*)(mblk + 16 * (p ^ (row & 7))), (void*)(smem + vbytes + q * 1024), 16, 0,
-                                     0);
-  }
-  const int s_lo = (KT * wave) / 4, s_hi = (KT * (wave + 1)) / 4;
-  const bool xon = r16 < M;
-  const v4i z4 = v4i{0, 0, 0, 0};
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  if constexpr (XL) {
-    // the M activation rows (M * K contiguous bytes) follow the weight block in
-    // LDS, swizzled the same way; rows >= M are never read (clamped, zeroed)
-    const int xchunks_row = K / 16, xoff = vbytes + mbytes;
-    for (int q = wave; q < (M * K) / 1024; q += 4) {
-      const int p = q * 64 + lane, row = p / xchunks_row;
-      __builtin_amdgcn_global_load_lds((void*)(xq + 16 * (p ^ (row & 7))), (void*)(smem + xoff + q * 1024), 16, 0,
-                                       0);
+
+  v4f acc0[RT], acc1[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc0[t] = acc1[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int u0 = wave; u0 < NU; u0 += NW) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int64_t n0 = (int64_t)(blockIdx.x * RT + t) * 16;
+      const uint8_t* vu = values + n0 * (K / 2) + u0 * (kUnitK / 2);
+      const uint8_t* mu = meta + n0 * (K / 8) + u0 * (kUnitK / 8);
+      uint8_t* rt = region + t * kUnitLds;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(vu + (int64_t)i * K + voff[i & 3]), (void*)(rt + i * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(mu + (int64_t)i * K + moff), (void*)(rt + 8192 + i * 1024), 16, 0, 0);
+    }
+    v8i b[8];
+    v4i x1;
+    if constexpr (X1) {
+      // one activation row: lane (r16, lg) holds chunk 8 (r16 >> 1) + 4 (r16 & 1) + lg
+      // of the unit, i.e. the half r16 & 1 of step r16 >> 1 that lane group lg needs
+      x1 = *reinterpret_cast<const v4i*>(xq + u0 * kUnitK + 128 * (r16 >> 1) + 64 * (r16 & 1) + 16 * lg);
+    } else {
+      const uint8_t* xp = xrow + u0 * kUnitK;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const v4i l = *reinterpret_cast<const v4i*>(xp + s * 128);
+        const v4i h = *reinterpret_cast<const v4i*>(xp + s * 128 + 64);
+        b[s] = __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
     wait_vmcnt<0>();
-    stage_barrier();
-    const int xr = min(r16, M - 1);
-    // groups of 4 steps: all LDS reads of a group first, then its MFMAs into
-    // two accumulators (so consecutive MFMAs do not wait on each other)
-    v4f acc2 = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = s_lo; s0 < s_hi; s0 += 4) {
-      v4i a[4], lo[4], hi[4];
-      int idx[4];
+    if constexpr (X1) {
+      // step s's operand: lanes 2s and 2s + 1 of each 16-lane row, broadcast
+      // to the whole row (DPP row_newbcast)
+      row_bcast_steps(b, x1, std::make_integer_sequence<int, 8>{});
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = min(s0 + u, s_hi - 1);
-        const int pv = r16 * vchunks_row + 4 * s + lg;
-        const int pm = r16 * mchunks_row + s;
-        const int px = xr * xchunks_row + 8 * s + lg;
-        a[u] = *reinterpret_cast<const v4i*>(smem + 16 * (pv ^ (r16 & 7)));
-        idx[u] = *reinterpret_cast<const int*>(smem + vbytes + 16 * (pm ^ (r16 & 7)) + 4 * lg);
-        lo[u] = *reinterpret_cast<const v4i*>(smem + xoff + 16 * (px ^ (xr & 7)));
-        hi[u] = *reinterpret_cast<const v4i*>(smem + xoff + 16 * ((px + 4) ^ (xr & 7)));
-      }
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool live = s0 + u < s_hi;
-        const v4i av = live ? a[u] : z4;
-        const v4i l = xon ? lo[u] : z4, h = xon ? hi[u] : z4;
-        const v8i b = v8i{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
-        if (u & 1) acc2 = smfmac16<XF, WF>(av, b, acc2, idx[u]);
-        else acc = smfmac16<XF, WF>(av, b, acc, idx[u]);
+      for (int t = 0; t < RT; ++t) {
+        const uint8_t* rt = region + t * kUnitLds;
+        const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
+        const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
+        if (s & 1) acc1[t] = smfmac16<XF, WF>(a, b[s], acc1[t], idx);
+        else acc0[t] = smfmac16<XF, WF>(a, b[s], acc0[t], idx);
       }
     }
-    acc += acc2;
-  } else {
-    // activation operands straight from memory, in chunks of SPW steps; the
-    // first chunk is in flight with the weight stream
-    constexpr int SPW = 8;
-    const uint8_t* xrow = xq + (int64_t)min(r16, M - 1) * K + 16 * lg;
-    v4i xlo[SPW], xhi[SPW];
-    auto load_x = [&](int c0) {
-#pragma unroll
-      for (int u = 0; u < SPW; ++u) {
-        const int64_t s = min(c0 + u, KT - 1);
-        xlo[u] = *reinterpret_cast<const v4i*>(xrow + s * 128);
-        xhi[u] = *reinterpret_cast<const v4i*>(xrow + s * 128 + 64);
-      }
-    };
-    load_x(s_lo);
-    wait_vmcnt<0>();
-    stage_barrier();
-    for (int c0 = s_lo; c0 < s_hi; c0 += SPW) {
-      if (c0 != s_lo) load_x(c0);
-#pragma unroll
-      for (int u = 0; u < SPW; ++u) {
-        const int s = c0 + u;
-        if (s < s_hi) {
-          const int pv = r16 * vchunks_row + 4 * s + lg;  // chunk of row r16, step s, lane group lg
-          const int pm = r16 * mchunks_row + s;            // metadata chunk of row r16, step s
-          const v4i a = *reinterpret_cast<const v4i*>(smem + 16 * (pv ^ (r16 & 7)));
-          const int idx = *reinterpret_cast<const int*>(smem + vbytes + 16 * (pm ^ (r16 & 7)) + 4 * lg);
-          const v4i lo = xon ? xlo[u] : z4, hi = xon ? xhi[u] : z4;
-          const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc = smfmac16<XF, WF>(a, b, acc, idx);
-        }
-      }
-    }
+    // the region's reads are complete (their values fed the MFMAs) before
+    // the next unit's loads overwrite it
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   }
-  // fixed-order reduction of the 4 partial tiles (LDS reused after a barrier)
-  stage_barrier();
-  v4f* red = reinterpret_cast<v4f*>(smem);
-  red[wave * 64 + lane] = acc;
+  // fixed-order reduction: each wavefront's partial tiles into its own region
+#pragma unroll
+  for (int t = 0; t < RT; ++t) reinterpret_cast<v4f*>(region)[t * 64 + lane] = acc0[t] + acc1[t];
   __syncthreads();
   if (wave == 0) {
-    v4f t = red[lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) t += red[w * 64 + lane];
-    v4f y;
+    for (int t = 0; t < RT; ++t) {
+      v4f sum = reinterpret_cast<const v4f*>(smem)[t * 64 + lane];
+      for (int w = 1; w < NW; ++w) sum += reinterpret_cast<const v4f*>(smem + w * (RT * kUnitLds))[t * 64 + lane];
+      v4f y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
-    if (bias) {
-      y[0] += bf16_to_f32(b2.x & 0xFFFFu);
-      y[1] += bf16_to_f32(b2.x >> 16);
-      y[2] += bf16_to_f32(b2.y & 0xFFFFu);
-      y[3] += bf16_to_f32(b2.y >> 16);
+      for (int i = 0; i < 4; ++i) y[i] = sum[i] * (xsm * w4[t][i]);
+      if (bias) {
+        y[0] += bf16_to_f32(b2[t].x & 0xFFFFu);
+        y[1] += bf16_to_f32(b2[t].x >> 16);
+        y[2] += bf16_to_f32(b2[t].y & 0xFFFFu);
+        y[3] += bf16_to_f32(b2[t].y >> 16);
+      }
+      if (m < M) store4<OUT>(out, N, m, (blockIdx.x * RT + t) * 16 + 4 * lg, y);
     }
-    if (m < M) store4<OUT>(out, N, m, n, y);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Dispatch
-// ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1>
-hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
-  using C = Tiled<BN, BM, WN, WM, S>;
-  const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
-  const int T = tiles_m * tiles_n;
-  const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC>;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride, a.ws_stride);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Decode with the activation quantization fused in (small M * K).
 // ---------------------------------------------------------------------------
 // One launch does both steps of the layer.  Every workgroup owns 16 weight
-// rows, as in the LDS-staged decode kernel, and first puts the loads of its
-// weight block into LDS in flight.  While they stream, it quantizes the whole
+// rows and first puts the loads of its whole weight block into LDS in flight.  While they stream, it quantizes the whole
 // (small) activation itself, exactly as quantize_rowwise_fp8 does: row maxima
 // of the bf16 magnitude bits by LDS atomic max (an exact, order-free maximum),
 // then scale, reciprocal and cast8 per 8 elements, the codes written straight
-// into the LDS activation stage (swizzled as the staged decode kernel reads
-// them) and the row scales into LDS for the epilogue.  Workgroup 0 also
+// into an LDS activation stage (each 16-byte chunk of a row at
+// chunk ^ (row & 7), as the weight block) and the row scales into LDS for the
+// epilogue.  Workgroup 0 also
 // writes the codes and scales to xq / xs.  No workgroup waits for another.
 // The redundant quantization costs about 20 ALU operations per element in
 // every workgroup, and its first LDS access waits for the weight block (the
@@ -941,7 +931,7 @@ __global__ __launch_bounds__(kFusedThreads) void linear_decode_fused_kernel(
   stage_barrier();
   const float xsm = rscale[min(m, M - 1)];
 
-  // 4. MFMAs over this wavefront's quarter of the k steps (as the LDS-staged kernel)
+  // 4. MFMAs over this wavefront's quarter of the k steps, operands from LDS
   const int s_lo = (KT * wave) / 4, s_hi = (KT * (wave + 1)) / 4;
   const bool xon = r16 < M;
   const v4i z4 = v4i{0, 0, 0, 0};
@@ -1034,23 +1024,56 @@ hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const Lin
 // ---------------------------------------------------------------------------
 // Kernel configurations ("algorithms") and the default choice by shape
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT>
-hipError_t run_decode_lds(const LinearArgs& a, hipStream_t stream) {
-  // the activation is staged in LDS too when it fits beside the weight block
-  constexpr int64_t kLds = 160 * 1024;
-  const bool xl = 10 * a.k + a.m * a.k <= kLds;
-  const unsigned lds = (unsigned)(10 * a.k + (xl ? a.m * a.k : 0));
-  auto kern = xl ? linear_decode_lds_kernel<XF, WF, OUT, true> : linear_decode_lds_kernel<XF, WF, OUT, false>;
-  static bool attr_set[2] = {false, false};  // benign race: every thread sets the same value
-  if (!attr_set[xl]) {
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1>
+hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
+  using C = Tiled<BN, BM, WN, WM, S>;
+  const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
+  const int T = tiles_m * tiles_n;
+  const int grid = 8 * ((T + 7) / 8);
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC>;
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
-    attr_set[xl] = true;
+    attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(256), lds, stream, a.xq, a.xs, a.values, a.meta, a.ws,
-                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws,
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride, a.ws_stride);
   return hipGetLastError();
+}
+
+// Wavefronts per workgroup of the unit decode kernel: the K / 1024 units
+// spread evenly over at most 8 wavefronts.
+inline int unit_waves(int64_t k) {
+  const int nu = (int)(k / kUnitK), per = (nu + 7) / 8;
+  return (nu + per - 1) / per;
+}
+
+template <int XF, int WF, int OUT, int RT, bool X1>
+hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
+  auto kern = linear_decode_unit_kernel<XF, WF, OUT, RT, X1>;
+  const int nw = unit_waves(a.k);
+  const unsigned lds = (unsigned)(nw * RT * kUnitLds);
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 8 * RT * kUnitLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / (16 * RT))), dim3(64 * nw), lds, stream, a.xq, a.xs, a.values,
+                     a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
+  return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT, int RT>
+hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
+  if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, RT, true>(a, stream);
+  return run_decode_unit_cfg<XF, WF, OUT, RT, false>(a, stream);
 }
 
 template <int XF, int WF, int OUT>
@@ -1073,11 +1096,12 @@ hipError_t run_decode_reg(const LinearArgs& a, hipStream_t stream) {
 template <int XF, int WF, int OUT>
 hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
   switch (algo) {
-    case ALGO_DECODE_LDS: return run_decode_lds<XF, WF, OUT>(a, stream);
+    case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, 1>(a, stream);
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
     case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
     case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
-    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 1>(a, stream);
+    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2>(a, stream);
+    case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
   }
 }
@@ -1092,31 +1116,38 @@ hipError_t run_out(const LinearArgs& a, int algo, hipStream_t stream) {
 
 const char* linear_algo_name(int algo) {
   static const char* const names[ALGO_COUNT] = {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128",
-                                                "tiled_256x256", "wide_256x256"};
+                                                "tiled_256x256", "wide_256x256", "decode_lds_32"};
   return algo >= 0 && algo < ALGO_COUNT ? names[algo] : nullptr;
 }
 
 bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
-  (void)n;
   switch (algo) {
-    case ALGO_DECODE_LDS: return m <= 16 && k % 1024 == 0 && 10 * k <= 160 * 1024;
+    case ALGO_DECODE_LDS: return m <= 16 && k % kUnitK == 0;
     case ALGO_DECODE_REG: return m <= 16;
     case ALGO_TILED_64:
     case ALGO_TILED_128:
     case ALGO_TILED_256: return true;
     case ALGO_WIDE_256: return k >= 4 * KSTEP;
+    case ALGO_DECODE_LDS_32: return m <= 16 && k % kUnitK == 0 && n % 32 == 0;
     default: return false;
   }
 }
 
-// The built-in choice: decode kernels up to 16 rows (LDS-staged when the
-// weight block fits), then the largest tile that still gives at least 256
-// (128, 64) or 512 (256) tiles, the pipelined kernel for 256 x 256 when K allows.
+// The built-in choice: up to 16 rows the unit decode kernel when K allows
+// (32 weight rows per workgroup for several activation rows and N >= 6144,
+// where the activation traffic it halves costs more than the workgroups it
+// gives up), else the register-streaming decode kernel; above 16 rows the
+// largest tile that still gives at least 256 (128, 64) or 512 (256) tiles;
+// for 256 x 256 the pipelined kernel from K = 6144 on (measured crossover:
+// 7% slower than the 8-wavefront kernel at K = 4096, 6% faster at K = 14336).
 int linear_default_algo(int64_t m, int64_t n, int64_t k) {
-  if (m <= 16) return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
+  if (m <= 16) {
+    if (m >= 2 && n >= 6144 && linear_algo_supported(ALGO_DECODE_LDS_32, m, n, k)) return ALGO_DECODE_LDS_32;
+    return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
+  }
   const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = ((m + 127) / 128) * ((n + 127) / 128);
-  if (big >= 512) return k >= 4 * KSTEP ? ALGO_WIDE_256 : ALGO_TILED_256;
+  if (big >= 512) return k >= 48 * KSTEP ? ALGO_WIDE_256 : ALGO_TILED_256;
   if (mid >= 256) return ALGO_TILED_128;
   return ALGO_TILED_64;
 }

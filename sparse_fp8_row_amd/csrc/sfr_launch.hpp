@@ -35,13 +35,14 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
 // Kernel configurations of the linear layer.  algo < 0: the built-in choice.
 enum LinearAlgo {
-  ALGO_DECODE_LDS = 0,  // m <= 16: 16 weight rows per workgroup, staged in LDS
-  ALGO_DECODE_REG = 1,  // m <= 16: 16 weight rows per workgroup, streamed to registers
-  ALGO_TILED_64 = 2,    // 64 x 64 tiles, 4 wavefronts
-  ALGO_TILED_128 = 3,   // 128 x 128 tiles, 4 wavefronts
-  ALGO_TILED_256 = 4,   // 256 x 256 tiles, 8 wavefronts
-  ALGO_WIDE_256 = 5,    // 256 x 256 tiles, 4 software-pipelined wavefronts (k >= 512)
-  ALGO_COUNT = 6
+  ALGO_DECODE_LDS = 0,     // m <= 16, k % 1024 == 0: 16 weight rows per workgroup, one 1024-k unit per wavefront via LDS
+  ALGO_DECODE_REG = 1,     // m <= 16: 16 weight rows per workgroup, streamed to registers
+  ALGO_TILED_64 = 2,       // 64 x 64 tiles, 4 wavefronts
+  ALGO_TILED_128 = 3,      // 128 x 128 tiles, 4 wavefronts
+  ALGO_TILED_256 = 4,      // 256 x 256 tiles, 8 wavefronts
+  ALGO_WIDE_256 = 5,       // 256 x 256 tiles, 4 software-pipelined wavefronts (k >= 512)
+  ALGO_DECODE_LDS_32 = 6,  // as ALGO_DECODE_LDS with 32 weight rows per workgroup (n % 32 == 0)
+  ALGO_COUNT = 7
 };
 const char* linear_algo_name(int algo);
 bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k);

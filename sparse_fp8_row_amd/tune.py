@@ -14,8 +14,9 @@ each shape on the current GPU and returns a table for
 
 Inputs are random FP8 codes (the kernels' speed does not depend on the
 values); timing is with HIP events on the current stream, after warm-up
-calls, with the weight rotated over enough copies that small shapes read HBM
-and batches long enough that launch latency does not set the time.
+calls, with the weight rotated over enough copies that small shapes read HBM,
+and small shapes' calls replayed from a HIP graph so that the host's launch
+rate does not set the time.
 """
 from __future__ import annotations
 
@@ -53,6 +54,47 @@ class _Inputs:
                       for _ in range(self.copies)]
 
 
+def graph_us(call, copies: int, calls: int = 0, replays: int = 0, min_ms: float = 2.0) -> float:
+    """Mean GPU microseconds per call of `call(i, stream_handle)` (i cycles over
+    `copies` weight copies), with the calls captured in one HIP graph and the
+    graph replayed, so that the host's launch rate does not set the time.
+
+    Every copy is used once eagerly (on a side stream) before the capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(copies):
+            call(i, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    calls = calls or max(copies, 64)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(calls):
+            call(i % copies, h)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def batch(r):
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(r):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    batch(1)
+    r = replays or 3
+    ms = batch(r)
+    if not replays and ms < min_ms:
+        r = int(r * min_ms / max(ms, 1e-3)) + 1
+        ms = batch(r)
+    del g
+    return ms * 1e3 / (r * calls)
+
+
 def time_algo(m: int, n: int, k: int, algo: int, x_dtype=torch.float8_e4m3fn, w_dtype=torch.float8_e4m3fn,
               reps: int = 20, warmup: int = 3, rotate_bytes: int = 600 << 20, stream=None,
               inputs: Optional[_Inputs] = None, min_ms: float = 2.0) -> float:
@@ -60,7 +102,9 @@ def time_algo(m: int, n: int, k: int, algo: int, x_dtype=torch.float8_e4m3fn, w_
 
     Every weight copy is used once before timing; the timed batch holds at
     least `reps` calls, every copy twice, and `min_ms` of GPU time, so that
-    the clocks have settled and short kernels are not timed by launch latency."""
+    the clocks have settled.  Up to 64 rows (kernels of a few microseconds)
+    the calls are timed inside a HIP graph, so that the host's launch rate
+    does not set the time."""
     inp = inputs if inputs is not None else _Inputs(m, n, k, x_dtype, w_dtype, rotate_bytes)
     lib = load()
     h = _stream(stream)
@@ -71,6 +115,16 @@ def time_algo(m: int, n: int, k: int, algo: int, x_dtype=torch.float8_e4m3fn, w_
             inp.xq.data_ptr(), xf, inp.xs.data_ptr(), SFR_SCALE_ROW, m, k, inp.vals[i].data_ptr(),
             inp.metas[i].data_ptr(), wf, inp.ws.data_ptr(), SFR_SCALE_ROW, n, None, inp.out.data_ptr(),
             SFR_OUT_BF16, algo, h), "sparse_fp8_scaled_linear_algo")
+
+    if stream is None and m <= 64:
+        # short kernels: time inside a graph (the host's launch rate would set
+        # an eager loop's pace)
+        def gcall(i, hs):
+            _check(lib.sparse_fp8_scaled_linear_algo(
+                inp.xq.data_ptr(), xf, inp.xs.data_ptr(), SFR_SCALE_ROW, m, k, inp.vals[i].data_ptr(),
+                inp.metas[i].data_ptr(), wf, inp.ws.data_ptr(), SFR_SCALE_ROW, n, None, inp.out.data_ptr(),
+                SFR_OUT_BF16, algo, hs), "sparse_fp8_scaled_linear_algo")
+        return graph_us(gcall, inp.copies, calls=max(reps, 2 * inp.copies), min_ms=min_ms)
 
     s = torch.cuda.current_stream() if stream is None else stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -164,20 +164,22 @@ def test_dynamic_linear_validation(lib):
 def test_linear_algos(lib):
     names = [lib.sfr_linear_algo_name(i) for i in range(lib.sfr_linear_algo_count())]
     assert names == [b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128", b"tiled_256x256",
-                     b"wide_256x256"]
-    assert lib.sfr_linear_algo_name(6) is None and lib.sfr_linear_algo_name(-1) is None
+                     b"wide_256x256", b"decode_lds_32"]
+    assert lib.sfr_linear_algo_name(7) is None and lib.sfr_linear_algo_name(-1) is None
     sup = lambda a, m, n, k: lib.sfr_linear_algo_supported(a, m, n, k)
     assert sup(0, 16, 4096, 4096) == 1 and sup(0, 17, 4096, 4096) == 0      # decode: m <= 16
-    assert sup(0, 4, 4096, 640) == 0                                        # LDS decode: k % 1024
-    assert sup(0, 4, 4096, 16384) == 1 and sup(0, 4, 4096, 17408) == 0      # weight block must fit LDS
+    assert sup(0, 4, 4096, 640) == 0 and sup(0, 4, 4096, 17408) == 1        # unit decode: k % 1024, any K
+    assert sup(6, 4, 4096, 1024) == 1 and sup(6, 4, 4112, 1024) == 0        # 32 rows per workgroup: n % 32
     assert sup(1, 16, 4096, 640) == 1 and sup(1, 17, 4096, 640) == 0
     assert all(sup(a, 5000, 4096, 256) == 1 for a in (2, 3, 4))
     assert sup(5, 5000, 4096, 384) == 0 and sup(5, 5000, 4096, 512) == 1   # pipelined: k >= 512
-    assert sup(2, 4, 100, 256) == 0 and sup(6, 4, 128, 256) == 0           # bad n, unknown id
+    assert sup(2, 4, 100, 256) == 0 and sup(7, 4, 128, 256) == 0           # bad n, unknown id
     # the built-in choice
     d = lib.sfr_linear_default_algo
-    assert d(1, 4096, 4096) == 0 and d(16, 4096, 14336) == 0 and d(16, 4096, 17408) == 1
-    assert d(8192, 14336, 4096) == 5 and d(8192, 14336, 256) == 4
+    assert d(1, 4096, 4096) == 0 and d(16, 4096, 14336) == 0 and d(16, 4096, 17408) == 0
+    assert d(1, 14336, 4096) == 0 and d(4, 14336, 4096) == 6 and d(16, 6144, 4096) == 6
+    assert d(16, 6144, 640) == 1 and d(4, 6160, 4096) == 0
+    assert d(8192, 14336, 4096) == 4 and d(8192, 14336, 6144) == 5 and d(8192, 14336, 256) == 4
     assert d(512, 14336, 4096) == 3 and d(512, 4096, 4096) == 2
 
 
@@ -191,7 +193,7 @@ def test_linear_algo_validation(lib):
         return f(a["xq"], a["xd"], a["xs"], a["xk"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["wk"],
                  a["n"], a["bias"], a["out"], a["od"], a["algo"], None)
 
-    assert call(algo=6) == DTYPE and call(algo=-2) == DTYPE
+    assert call(algo=7) == DTYPE and call(algo=-2) == DTYPE
     assert call(algo=0) == SHAPE                  # k = 256: not a multiple of 1024
     assert call(algo=5) == SHAPE                  # k < 512
     assert call(algo=1, xq=None) == NULL          # supported: validation goes on

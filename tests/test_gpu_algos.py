@@ -17,7 +17,11 @@ pytestmark = pytest.mark.gpu
 
 E4, E5 = oracle.E4M3, oracle.E5M2
 SHAPES = [("all_algos", 7, 1040, 1024, E4, E4, True), ("tiled", 300, 4112, 640, E5, E4, True),
-          ("max_k_decode", 16, 256, 16384, E4, E5, False)]
+          ("max_k_decode", 16, 256, 16384, E4, E5, False),
+          # one activation row, 7 wavefronts of 2 units each, 16 and 32 rows per workgroup
+          ("decode_one_row", 1, 6144, 14336, E5, E4, True),
+          # 20 units over 7 wavefronts (3, 3, ..., 2), several activation rows
+          ("decode_uneven_units", 5, 2080, 20480, E4, E4, False)]
 
 
 @pytest.fixture(scope="module", autouse=True)

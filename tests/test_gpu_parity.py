@@ -150,8 +150,8 @@ RAGGED = [
     sfr_inputs.Case("ragged", 6, 1000, 4112, 256, x_fmt=E4, w_fmt=E4, bias=True),
     sfr_inputs.Case("ragged", 6, 4100, 8208, 256, x_fmt=E5, w_fmt=E5),
     sfr_inputs.Case("ragged", 6, 2, 144, 128, x_fmt=E4, w_fmt=E4, bias=True),
-    # decode kernels: LDS-staged with and without the activation in LDS, and
-    # the largest K whose weight block fills the whole LDS
+    # decode kernels: one 1024-k unit per wavefront (one and several units per
+    # wavefront, the single-row activation path), K beyond one unit per wavefront
     sfr_inputs.Case("ragged", 6, 3, 64, 1024, x_fmt=E5, w_fmt=E4, bias=True),
     sfr_inputs.Case("ragged", 6, 16, 32, 16384, x_fmt=E4, w_fmt=E5),
     sfr_inputs.Case("ragged", 6, 1, 48, 16384, x_fmt=E5, w_fmt=E5, bias=True),
