@@ -16,6 +16,8 @@ Sources, cited per function in ``sfr_oracle.c``:
     the four FP8 dtype pairs.
   * "[float8nocompile] ... atomic_max-based algo ..." (pytorch/ao PR #1455):
     deterministic amax.
+  * "promote blocksparse from prototype, make it faster" (pytorch/ao PR
+    #1734): the block-sparse (BSR, 64 x 64 blocks) weight and its linear layer.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against library routines, closed forms, brute force and printed fixtures.
@@ -79,10 +81,15 @@ def _load():
             "orc_prune_2to4": [P, I64, I64, P],
             "orc_check_all_groups": [P, P],
             "orc_linear": [P, I, P, I64, I64, P, P, I, P, I64, P, P, I64, P, I64, P, P, P],
+            "orc_bsr_fill": [P, I64, I64, I64, P, P, P],
+            "orc_bsr_to_dense": [P, P, P, I64, I64, I64, P],
+            "orc_bsr_linear": [P, I64, I64, P, P, P, I64, I64, P, P, I64, P, I64, P, P, P],
         }.items():
             fn = getattr(lib, name)
             fn.restype = None
             fn.argtypes = args
+        lib.orc_bsr_count.restype = I64
+        lib.orc_bsr_count.argtypes = [P, I64, I64, I64, P]
         lib.orc_num_threads.restype = I
         lib.orc_num_threads.argtypes = []
         _lib = lib
@@ -240,4 +247,61 @@ def linear(xq, xfmt, xs, values, meta, wfmt, ws, bias=None, rows=None, cols=None
     _load().orc_linear(_ptr(xq), xfmt, _ptr(xs), m, k, _ptr(values), _ptr(meta), wfmt, _ptr(ws), n,
                        None if bias is None else _ptr(bias), _ptr(rows), len(rows), _ptr(cols),
                        len(cols), _ptr(y), _ptr(acc), _ptr(sabs))
+    return {"y": y, "acc32": acc, "sabs": sabs, "bf16": bf16_from_double(y)}
+
+
+# --------------------------------------------------------------------------
+# Block-sparse (BSR) weight, blocks of 64 x 64
+# --------------------------------------------------------------------------
+BSR_BLOCK = 64
+
+
+def bsr_from_dense(w_bf16: np.ndarray, bs: int = BSR_BLOCK):
+    """(crow int32 [n/bs + 1], col int32 [nnz], values uint16 [nnz, bs, bs]) of
+    bf16 bits [n, k]: the blocks holding any non-zero value, in block-row order
+    and ascending block column."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    assert n % bs == 0 and k % bs == 0
+    crow = np.empty(n // bs + 1, np.int32)
+    nnz = int(_load().orc_bsr_count(_ptr(w), n, k, bs, _ptr(crow)))
+    col = np.empty(nnz, np.int32)
+    values = np.empty((nnz, bs, bs), np.uint16)
+    _load().orc_bsr_fill(_ptr(w), n, k, bs, _ptr(crow), _ptr(col), _ptr(values))
+    return crow, col, values
+
+
+def bsr_to_dense(crow, col, values, n: int, k: int) -> np.ndarray:
+    crow = np.ascontiguousarray(crow, np.int32)
+    col = np.ascontiguousarray(col, np.int32)
+    values = np.ascontiguousarray(values, np.uint16)
+    bs = values.shape[1] if values.ndim == 3 else BSR_BLOCK
+    w = np.empty((n, k), np.uint16)
+    _load().orc_bsr_to_dense(_ptr(crow), _ptr(col), _ptr(values), n, k, bs, _ptr(w))
+    return w
+
+
+def bsr_linear(x_bf16, crow, col, values, n: int, bias=None, rows=None, cols=None):
+    """out[m, n] = sum_k x[m, k] * W[n, k] (+ bias[n]) for the BSR weight W.
+
+    Returns a dict of [len(rows), len(cols)] arrays: y (binary64 sum), acc32
+    (serial binary32 sum, no bias), sabs (sum |x * w|), bf16 (y rounded once)."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    crow = np.ascontiguousarray(crow, np.int32)
+    col = np.ascontiguousarray(col, np.int32)
+    values = np.ascontiguousarray(values, np.uint16)
+    m, k = x.shape
+    bs = BSR_BLOCK
+    assert crow.shape == (n // bs + 1,) and values.shape == (len(col), bs, bs)
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    cols = np.arange(n, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+    y = np.empty((len(rows), len(cols)), np.float64)
+    acc = np.empty((len(rows), len(cols)), np.float32)
+    sabs = np.empty((len(rows), len(cols)), np.float64)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, np.uint16)
+        assert bias.shape == (n,)
+    _load().orc_bsr_linear(_ptr(x), m, k, _ptr(crow), _ptr(col), _ptr(values), n, bs,
+                           None if bias is None else _ptr(bias), _ptr(rows), len(rows), _ptr(cols), len(cols),
+                           _ptr(y), _ptr(acc), _ptr(sabs))
     return {"y": y, "acc32": acc, "sabs": sabs, "bf16": bf16_from_double(y)}

@@ -15,6 +15,12 @@
  *       (activation, weight) dtype pairs e4m3/e5m2 x e4m3/e5m2.
  *  [P5] "[float8nocompile] ... atomic_max-based algo ..." (PR #1455), review
  *       thread: the amax reduction should stay deterministic.
+ *  [P2] "promote blocksparse from prototype, make it faster" (PR #1734): a
+ *       weight stored block-sparse (BSR) with blocks of 64 x 64 and most
+ *       blocks zero (sparsity level 0.9 in its numbers), multiplied by a
+ *       dense activation whose decode row count is padded up to 16.  The page
+ *       names no number format; read here as the model's bf16 weight and
+ *       activation with a binary32-or-better sum and a bf16 result.
  * The formats' constants (e4m3 max 448, e5m2 max 57344) are the OCP FP8
  * definitions; the pages only name the dtypes.
  *
@@ -364,6 +370,107 @@ void orc_linear(const uint8_t* xq, int xfmt, const float* xs, int64_t m, int64_t
             y_exact[i * nc + j] = y;
             acc32[i * nc + j] = f;
             sabs[i * nc + j] = ldexp((double)sa, -fb) * t;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Block-sparse (BSR) weight and linear layer.  [P2]: blocks of bs x bs        */
+/* (bs = 64 there), stored as the usual compressed-sparse-row structure over  */
+/* blocks: crow (block-row pointers), col (block-column indices) and the      */
+/* kept blocks' values.                                                       */
+/* ------------------------------------------------------------------------- */
+
+/* A bs x bs block of w[n, k] (bf16 bits, row-major) at block row br and block
+ * column bc is kept when any element is non-zero by value: +0.0 (0x0000) and
+ * -0.0 (0x8000) both count as zero, every other code (subnormals, NaN, inf
+ * included) as non-zero. */
+static int bsr_block_kept(const uint16_t* w, int64_t k, int64_t bs, int64_t br, int64_t bc)
+{
+    for (int64_t r = 0; r < bs; ++r)
+        for (int64_t c = 0; c < bs; ++c)
+            if ((w[(br * bs + r) * k + bc * bs + c] & 0x7FFF) != 0) return 1;
+    return 0;
+}
+
+/* crow[0 .. n/bs]: crow[0] = 0 and crow[i + 1] = crow[i] + (number of kept
+ * blocks in block row i).  Returns the total number of kept blocks. */
+int64_t orc_bsr_count(const uint16_t* w, int64_t n, int64_t k, int64_t bs, int32_t* crow)
+{
+    int64_t nbr = n / bs, nbc = k / bs, total = 0;
+    crow[0] = 0;
+    for (int64_t br = 0; br < nbr; ++br) {
+        for (int64_t bc = 0; bc < nbc; ++bc) total += bsr_block_kept(w, k, bs, br, bc);
+        crow[br + 1] = (int32_t)total;
+    }
+    return total;
+}
+
+/* col[crow[i] ..]: the kept block columns of block row i in ascending order;
+ * values[j]: block j copied as bs x bs row-major bf16 bits. */
+void orc_bsr_fill(const uint16_t* w, int64_t n, int64_t k, int64_t bs, const int32_t* crow, int32_t* col,
+                  uint16_t* values)
+{
+    int64_t nbr = n / bs, nbc = k / bs;
+    for (int64_t br = 0; br < nbr; ++br) {
+        int64_t j = crow[br];
+        for (int64_t bc = 0; bc < nbc; ++bc) {
+            if (!bsr_block_kept(w, k, bs, br, bc)) continue;
+            col[j] = (int32_t)bc;
+            for (int64_t r = 0; r < bs; ++r)
+                for (int64_t c = 0; c < bs; ++c)
+                    values[(j * bs + r) * bs + c] = w[(br * bs + r) * k + bc * bs + c];
+            ++j;
+        }
+    }
+}
+
+/* The dense matrix the structure describes: zero outside the kept blocks. */
+void orc_bsr_to_dense(const int32_t* crow, const int32_t* col, const uint16_t* values, int64_t n, int64_t k,
+                      int64_t bs, uint16_t* w)
+{
+    memset(w, 0, (size_t)(n * k) * sizeof(uint16_t));
+    for (int64_t br = 0; br < n / bs; ++br)
+        for (int64_t j = crow[br]; j < crow[br + 1]; ++j)
+            for (int64_t r = 0; r < bs; ++r)
+                for (int64_t c = 0; c < bs; ++c)
+                    w[(br * bs + r) * k + (int64_t)col[j] * bs + c] = values[(j * bs + r) * bs + c];
+}
+
+/* out[r, c] = sum_k x[r, k] * W[c, k] (+ bias[c]) for the BSR weight W, at the
+ * positions (rows[i], cols[j]).  The sum runs over the kept blocks of block
+ * row c / bs in stored order and, inside a block, over ascending k, in
+ * binary64 (each bf16 x bf16 product is exact in binary64; zero blocks add
+ * nothing, so this is the dense definition).  Also returns
+ * sabs = sum |x * w| (the tolerance scale) and acc32, the same sum taken
+ * serially in binary32 (without bias). */
+void orc_bsr_linear(const uint16_t* x, int64_t m, int64_t k, const int32_t* crow, const int32_t* col,
+                    const uint16_t* values, int64_t n, int64_t bs, const uint16_t* bias, const int64_t* rows,
+                    int64_t nr, const int64_t* cols, int64_t nc, double* y, float* acc32, double* sabs)
+{
+    (void)m;
+    (void)n;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t j = 0; j < nc; ++j) {
+        int64_t c = cols[j], br = c / bs, rin = c % bs;
+        for (int64_t i = 0; i < nr; ++i) {
+            const uint16_t* xr = x + rows[i] * k;
+            double s = 0.0, sa = 0.0;
+            float f = 0.0f;
+            for (int64_t b = crow[br]; b < crow[br + 1]; ++b) {
+                const uint16_t* wr = values + (b * bs + rin) * bs;
+                const uint16_t* xb = xr + (int64_t)col[b] * bs;
+                for (int64_t kk = 0; kk < bs; ++kk) {
+                    double p = (double)orc_bf16_to_float(xb[kk]) * (double)orc_bf16_to_float(wr[kk]);
+                    s += p;
+                    sa += fabs(p);
+                    f = f + (float)p;   /* the product is exact in binary32 too */
+                }
+            }
+            if (bias) s = s + (double)orc_bf16_to_float(bias[c]);
+            y[i * nc + j] = s;
+            acc32[i * nc + j] = f;
+            sabs[i * nc + j] = sa;
         }
     }
 }
