@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GB/s measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-algo-search", action="store_true", help="skip the per-shape kernel configuration search")
+    p.add_argument("--no-bsr", action="store_true", help="skip the block-sparse (BSR) decode measurement")
     p.add_argument("--cpu-rows", type=int, default=160, help="activation rows in the CPU oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (for scaling HBM byte counters) and exit")
@@ -232,6 +233,9 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(torch, sfr, sfr_inputs, lib, dev, stream)
 
+    if not args.no_bsr:
+        result["bsr_decode"] = bench_bsr(torch, sfr, sfr_inputs, dev)
+
     if not args.no_algo_search:
         result["algo_search"] = bench_algo_search()
 
@@ -282,6 +286,64 @@ def bench_tensorwise(torch, sfr, lib, w, x, M, N, K, h, stream, steps=20, warmup
             "TFLOP/s": round(2.0 * M * N * K / (step_ms * 1e-3) / 1e12, 2),
             "kernels_ms": {"quantize_tensorwise": round(q_ms, 5), "gemm": round(g_ms, 5)},
             "quantize_gbs": round(quant_bytes(M, K) / (q_ms * 1e-3) / 1e9, 1)}
+
+
+def bsr_bytes(m, n, k, nnz, bias):
+    """Algorithmic bytes of one BSR linear call: kept blocks, their column
+    indices, the block-row pointers, bf16 activation and output (and bias)."""
+    return nnz * 64 * 64 * 2 + 4 * nnz + 4 * (n // 64 + 1) + 2 * m * k + 2 * m * n + (2 * n if bias else 0)
+
+
+def bench_bsr(torch, sfr, sfr_inputs, dev):
+    """Block-sparse (64 x 64 blocks, sparsity 0.9) bf16 decode at M in {1, 4, 16}
+    on the Llama-3.1-8B o-projection (N = K = 4096) and up-projection
+    (N = 14336, K = 4096) shapes, bf16 bias: per call from a HIP graph,
+    rotating over >= 600 MB of weight copies; beside it the dense bf16 layer
+    (torch.matmul, same rotation and graph timing) as the reference the pages
+    compare against."""
+    from sparse_fp8_row_amd import tune
+    res = {}
+    for shape in ("o", "up"):
+        n, k = sfr_inputs.LLAMA_SHAPES[shape]
+        case = sfr_inputs.Case("bsr_bench", 30, 16, n, k, bias=True)
+        wb = sfr_inputs.draw_bsr_w(case)
+        w = torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16)
+        base = sfr.bsr_from_dense(w)
+        bias = torch.from_numpy(sfr_inputs.draw_bias(case).view(np.int16)).to(dev).view(torch.bfloat16)
+        per = base.values.numel() * 2
+        copies = max(2, int(np.ceil(600e6 / max(per, 1))))
+        weights = [base] + [sfr.BsrWeight(base.crow, base.col, base.values.clone(), n, k) for _ in range(copies - 1)]
+        dcopies = max(2, int(np.ceil(600e6 / (2 * n * k))))
+        wt = w.t().contiguous()  # [K, N]: the dense product takes a contiguous right operand
+        dense = [wt] + [wt.clone() for _ in range(dcopies - 1)]
+        for m in (1, 4, 16):
+            x = torch.from_numpy(sfr_inputs.draw_x(sfr_inputs.Case("bsr_bench", 30, m, n, k)).view(np.int16)) \
+                .to(dev).view(torch.bfloat16)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            lib = sfr.load()
+
+            def call(i, hs):
+                bw = weights[i]
+                st = lib.bsr_linear_bf16(x.data_ptr(), m, k, bw.crow.data_ptr(), bw.col.data_ptr(),
+                                         bw.values.data_ptr(), n, bias.data_ptr(), out.data_ptr(), sfr.SFR_OUT_BF16, hs)
+                assert st == 0, st
+
+            dout = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+            def dcall(i, hs):
+                torch.addmm(bias, x, dense[i], out=dout)
+
+            us = tune.graph_us(call, copies, calls=2 * copies)
+            dus = tune.graph_us(dcall, dcopies, calls=2 * dcopies)
+            b = bsr_bytes(m, n, k, base.nnz, True)
+            gbs = b / (us * 1e-6) / 1e9
+            res[f"{shape}_M{m}"] = {"us_per_call": round(us, 3), "bytes": b, "GB/s": round(gbs, 1),
+                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "nnz_blocks": base.nnz,
+                                    "dense_bf16_torch_us": round(dus, 3), "speedup_vs_dense": round(dus / us, 2)}
+            print(f"[bench] bsr {shape} M={m}: {us:.3f} us/call ({gbs:.1f} GB/s), dense bf16 (torch) {dus:.3f} us, "
+                  f"x{dus / us:.2f}", file=sys.stderr, flush=True)
+        del weights, dense, wt
+    return res
 
 
 def bench_algo_search():

@@ -266,6 +266,52 @@ sfr_status sparse_fp8_scaled_linear_algo(const uint8_t* xq, sfr_fp8_t x_dt, cons
                                          const uint16_t* bias, void* out, sfr_out_t out_dt, int algo,
                                          void* stream);
 
+/*
+ * Block-sparse (BSR) bf16 weight and its linear layer.
+ * Source: pytorch/ao PR #1734 ("promote blocksparse from prototype, make it
+ * faster"): the weight is stored in blocks of 64 x 64, most of them zero
+ * (its measurements use sparsity level 0.9), and multiplied by a dense
+ * activation whose row count is padded to 16 for decode.  The page names no
+ * number format; here weight, activation and output are bf16, the sum is
+ * binary32 (every bf16 product is exact in it), the result rounded once to
+ * bf16 (nearest, ties to even) or returned in binary32.
+ *
+ * Layout (compressed-sparse-row over blocks, as torch's BSR tensors):
+ *   crow   int32 [n/64 + 1]: crow[0] = 0, crow[i+1] - crow[i] = kept blocks of
+ *          block row i (rows 64 i .. 64 i + 63); nnz = crow[n/64].
+ *   col    int32 [nnz]: block column of each kept block, ascending within a
+ *          block row.
+ *   values bf16 bits [nnz][64][64]: each kept block, row-major.
+ * A block is kept when any element is non-zero by value (+0.0 and -0.0 are
+ * zero; NaN, infinities and subnormals are non-zero).
+ *
+ * bsr_count_bf16(w, n, k, crow, stream): two launches write crow for the
+ *   dense bf16 w [n, k] (row-major, 16-byte aligned).  The caller reads
+ *   crow[n/64] (nnz) to size col and values.
+ * bsr_fill_bf16(w, n, k, crow, col, values, stream): writes col and values
+ *   for the crow that bsr_count_bf16 wrote for the same w.  col and values
+ *   may be NULL only when nnz = 0.
+ * bsr_linear_bf16(x, m, k, crow, col, values, n, bias, out, out_dt, stream):
+ *   out[m, n] = sum_k x[i, k] W[j, k] (+ bias[j]) for bf16 x [m, k]
+ *   (row-major), the BSR weight W [n, k] and optional bf16 bias [n]; out is
+ *   bf16 or binary32 [m, n], row-major.  Deterministic (fixed summation
+ *   order).  Every block column index is clamped to the matrix, but crow and
+ *   the values array must be the ones bsr_count_bf16 / bsr_fill_bf16 wrote
+ *   (they are read as given).
+ * Sizes: 0 <= n, m <= SFR_MAX_DIM; 0 < k <= SFR_MAX_DIM; n % 64 == 0,
+ * k % 64 == 0.  Alignment: w, x, values, bias, out 16 bytes; crow, col 4.
+ * Errors: SFR_ERR_SHAPE, SFR_ERR_NULL, SFR_ERR_ALIGN, SFR_ERR_DTYPE (out_dt),
+ * SFR_ERR_LAUNCH.  All pointers are device memory owned by the caller; the
+ * calls are asynchronous on `stream` (NULL = the default stream).
+ */
+#define SFR_BSR_BLOCK 64
+sfr_status bsr_count_bf16(const uint16_t* w, int64_t n, int64_t k, int32_t* crow, void* stream);
+sfr_status bsr_fill_bf16(const uint16_t* w, int64_t n, int64_t k, const int32_t* crow, int32_t* col,
+                         uint16_t* values, void* stream);
+sfr_status bsr_linear_bf16(const uint16_t* x, int64_t m, int64_t k, const int32_t* crow, const int32_t* col,
+                           const uint16_t* values, int64_t n, const uint16_t* bias, void* out, sfr_out_t out_dt,
+                           void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sfr_status_string(sfr_status s);
 

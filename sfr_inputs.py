@@ -143,3 +143,41 @@ def draw_bias(case: Case) -> Optional[np.ndarray]:
         return None
     g = _rng(case.seed, case.cfg_id, T_BIAS)
     return to_bf16_bits(g.normal(0.0, 0.01, size=case.n))
+
+
+# --------------------------------------------------------------------------
+# Block-sparse (BSR) workload ("promote blocksparse from prototype, make it
+# faster", pytorch/ao PR #1734): 64 x 64 blocks, sparsity level 0.9, Llama
+# shapes, decode batches padded up to 16 rows.  The generator draws a dense
+# bf16 weight ~N(0, 0.02) and zeroes every block outside a seeded choice of
+# round(keep * blocks) blocks (chosen over the whole matrix, so block rows keep
+# different numbers of blocks); with ``special`` some dropped blocks hold -0.0
+# entries and one kept block holds a single subnormal.  Stream ids: mask 6,
+# special entries 7 (weight values use T_W, activations T_X, bias T_BIAS).
+# --------------------------------------------------------------------------
+T_BLOCKMASK, T_BLOCKSPECIAL = 6, 7
+BSR_BLOCK = 64
+BSR_SPARSITY = 0.9
+
+
+def draw_bsr_w(case: Case, sparsity: float = BSR_SPARSITY, special: bool = False) -> np.ndarray:
+    """Block-sparse weight as bf16 bits [N, K] (N, K multiples of 64)."""
+    n, k, bs = case.n, case.k, BSR_BLOCK
+    assert n % bs == 0 and k % bs == 0
+    w = draw_w(Case(case.cfg, case.cfg_id, case.m, n, k, seed=case.seed))
+    nb = (n // bs) * (k // bs)
+    keep = int(round((1.0 - sparsity) * nb))
+    kept = np.zeros(nb, bool)
+    kept[_rng(case.seed, case.cfg_id, T_BLOCKMASK).choice(nb, size=keep, replace=False)] = True
+    kept = kept.reshape(n // bs, k // bs)
+    w = np.where(np.kron(kept, np.ones((bs, bs), bool)), w, np.uint16(0))
+    if special:
+        g = _rng(case.seed, case.cfg_id, T_BLOCKSPECIAL)
+        dropped = np.argwhere(~kept)
+        for br, bc in dropped[: max(1, len(dropped) // 10)]:
+            blk = w[br * bs:(br + 1) * bs, bc * bs:(bc + 1) * bs]
+            blk[g.random((bs, bs)) < 0.2] = 0x8000
+        if len(dropped) > 1:
+            br, bc = dropped[-1]
+            w[br * bs + 3, bc * bs + 60] = 0x0001
+    return np.ascontiguousarray(w)

@@ -38,7 +38,7 @@ EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_ten
             "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
             "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count",
             "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
-            "sfr_status_string", "sfr_format_version")
+            "bsr_count_bf16", "bsr_fill_bf16", "bsr_linear_bf16", "sfr_status_string", "sfr_format_version")
 
 _FP8 = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
 _lib = None
@@ -75,8 +75,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sfr_linear_algo_supported.restype = I
     lib.sfr_linear_default_algo.argtypes = [I64, I64, I64]
     lib.sfr_linear_default_algo.restype = I
+    lib.bsr_count_bf16.argtypes = [P, I64, I64, P, P]
+    lib.bsr_fill_bf16.argtypes = [P, I64, I64, P, P, P, P]
+    lib.bsr_linear_bf16.argtypes = [P, I64, I64, P, P, P, I64, P, P, I, P]
     for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
-               lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic):
+               lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic,
+               lib.bsr_count_bf16, lib.bsr_fill_bf16, lib.bsr_linear_bf16):
         fn.restype = I
     lib.sfr_quantize_tensorwise_workspace_bytes.argtypes = [I64, I64]
     lib.sfr_quantize_tensorwise_workspace_bytes.restype = I64
@@ -332,3 +336,65 @@ def linear(x: torch.Tensor, w: SparseFp8Weight, bias: Optional[torch.Tensor] = N
     else:
         raise ValueError("act_scaling must be 'row' or 'tensor'")
     return sparse_fp8_scaled_linear(xq, xs, w.values, w.meta, w.scale, bias, stream=stream)
+
+
+# --------------------------------------------------------------------------
+# Block-sparse (BSR, 64 x 64 blocks) bf16 weight
+# --------------------------------------------------------------------------
+BSR_BLOCK = 64
+
+
+@dataclass
+class BsrWeight:
+    """A bf16 weight [n, k] in block-sparse form: crow int32 [n/64 + 1], col
+    int32 [nnz], values bf16 [nnz, 64, 64] (torch's BSR layout)."""
+    crow: torch.Tensor
+    col: torch.Tensor
+    values: torch.Tensor
+    n: int
+    k: int
+
+    @property
+    def nnz(self) -> int:
+        return self.col.shape[0]
+
+
+def bsr_from_dense(w: torch.Tensor, stream=None) -> BsrWeight:
+    """Dense bf16 [n, k] -> BsrWeight keeping every 64 x 64 block that holds a
+    non-zero value (two kernels, a read of the block count, one kernel)."""
+    _dev(w, "w")
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("w must be a 2-D bfloat16 tensor")
+    n, k = w.shape
+    lib, h = load(), _stream(stream)
+    crow = torch.empty((n // BSR_BLOCK + 1,), dtype=torch.int32, device=w.device)
+    _check(lib.bsr_count_bf16(w.data_ptr(), n, k, crow.data_ptr(), h), "bsr_count_bf16")
+    nnz = int(crow[-1].item()) if crow.numel() else 0
+    col = torch.empty((nnz,), dtype=torch.int32, device=w.device)
+    values = torch.empty((nnz, BSR_BLOCK, BSR_BLOCK), dtype=torch.bfloat16, device=w.device)
+    _check(lib.bsr_fill_bf16(w.data_ptr(), n, k, crow.data_ptr(), col.data_ptr() if nnz else None,
+                             values.data_ptr() if nnz else None, h), "bsr_fill_bf16")
+    return BsrWeight(crow, col, values, n, k)
+
+
+def bsr_linear(x: torch.Tensor, w: BsrWeight, bias: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bf16 x [m, k] -> out [m, n] = x @ W^T (+ bias) for the BSR weight W."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != w.k:
+        raise ValueError("x must be bfloat16 [m, k]")
+    m = x.shape[0]
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.shape != (w.n,):
+            raise ValueError("bias must be bfloat16 [n]")
+    od = {torch.bfloat16: SFR_OUT_BF16, torch.float32: SFR_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    elif out.shape != (m, w.n) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(load().bsr_linear_bf16(x.data_ptr(), m, w.k, w.crow.data_ptr(), w.col.data_ptr() if w.nnz else None,
+                                  w.values.data_ptr() if w.nnz else None, w.n,
+                                  None if bias is None else bias.data_ptr(), out.data_ptr(), od, _stream(stream)),
+           "bsr_linear_bf16")
+    return out

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_fp8_row.so")
-SOURCES = ["api.hip", "quantize.hip", "compress.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "compress.hip", "gemm.hip", "bsr.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -130,6 +130,45 @@ sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const fl
                                   out, out_dt, stream);
 }
 
+sfr_status bsr_count_bf16(const uint16_t* w, int64_t n, int64_t k, int32_t* crow, void* stream) {
+  if (n < 0 || n > SFR_MAX_DIM || n % SFR_BSR_BLOCK != 0 || k <= 0 || k > SFR_MAX_DIM || k % SFR_BSR_BLOCK != 0 ||
+      n * k > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (!crow || (n > 0 && !w)) return SFR_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(crow) & 3u) || (w && !aligned16(w))) return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_bsr_count(w, n, k, crow, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status bsr_fill_bf16(const uint16_t* w, int64_t n, int64_t k, const int32_t* crow, int32_t* col,
+                         uint16_t* values, void* stream) {
+  if (n < 0 || n > SFR_MAX_DIM || n % SFR_BSR_BLOCK != 0 || k <= 0 || k > SFR_MAX_DIM || k % SFR_BSR_BLOCK != 0 ||
+      n * k > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (n == 0) return SFR_OK;
+  if (!w || !crow) return SFR_ERR_NULL;
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(crow) & 3u) || (reinterpret_cast<uintptr_t>(col) & 3u) ||
+      (values && !aligned16(values)))
+    return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_bsr_fill(w, n, k, crow, col, values, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status bsr_linear_bf16(const uint16_t* x, int64_t m, int64_t k, const int32_t* crow, const int32_t* col,
+                           const uint16_t* values, int64_t n, const uint16_t* bias, void* out, sfr_out_t out_dt,
+                           void* stream) {
+  if (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32) return SFR_ERR_DTYPE;
+  if (m < 0 || m > SFR_MAX_DIM || n < 0 || n > SFR_MAX_DIM || n % SFR_BSR_BLOCK != 0 || k <= 0 ||
+      k > SFR_MAX_DIM || k % SFR_BSR_BLOCK != 0 || m * k > kMaxElems || n * k > kMaxElems || m * n > kMaxElems ||
+      (n / 16) * ((m + 15) / 16) > INT32_MAX)
+    return SFR_ERR_SHAPE;
+  if (m == 0 || n == 0) return SFR_OK;
+  if (!x || !crow || !out) return SFR_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(crow) & 3u) || (reinterpret_cast<uintptr_t>(col) & 3u) ||
+      (values && !aligned16(values)) || !aligned16(out) || (bias && !aligned16(bias)))
+    return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_bsr_linear(x, m, k, crow, col, values, n, bias, out, (int)out_dt,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* sfr_status_string(sfr_status s) {
   switch (s) {
     case SFR_OK: return "ok";

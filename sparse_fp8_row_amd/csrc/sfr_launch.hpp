@@ -54,4 +54,12 @@ hipError_t launch_linear_algo(const LinearArgs& a, int algo, hipStream_t stream)
 hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a,
                                  hipStream_t stream);
 
+// Block-sparse (BSR, 64 x 64 blocks) bf16 weight.
+hipError_t launch_bsr_count(const uint16_t* w, int64_t n, int64_t k, int32_t* crow, hipStream_t stream);
+hipError_t launch_bsr_fill(const uint16_t* w, int64_t n, int64_t k, const int32_t* crow, int32_t* col,
+                           uint16_t* values, hipStream_t stream);
+hipError_t launch_bsr_linear(const uint16_t* x, int64_t m, int64_t k, const int32_t* crow, const int32_t* col,
+                             const uint16_t* values, int64_t n, const uint16_t* bias, void* out, int out_fmt,
+                             hipStream_t stream);
+
 }  // namespace sfr

@@ -30,7 +30,8 @@ def test_header_declares_the_api():
     for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
               "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
               "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo",
-              "sfr_linear_algo_count", "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo"):
+              "sfr_linear_algo_count", "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
+              "bsr_count_bf16", "bsr_fill_bf16", "bsr_linear_bf16"):
         assert n in names
 
 
@@ -210,3 +211,32 @@ def test_binding_rejects_host_tensors():
     import sparse_fp8_row_amd as sfr
     with pytest.raises(ValueError):
         sfr.quantize_rowwise_fp8(torch.zeros((2, 16), dtype=torch.bfloat16))
+
+
+def test_bsr_validation(lib):
+    c, fl, li = lib.bsr_count_bf16, lib.bsr_fill_bf16, lib.bsr_linear_bf16
+    assert c(A, 96, 128, A, None) == SHAPE               # n % 64
+    assert c(A, 64, 100, A, None) == SHAPE               # k % 64
+    assert c(A, 64, 0, A, None) == SHAPE
+    assert c(A, -64, 64, A, None) == SHAPE
+    assert c(A, 64, 64, None, None) == NULL
+    assert c(None, 64, 64, A, None) == NULL
+    assert c(U, 64, 64, A, None) == ALIGN
+    assert c(A, 64, 64, A + 2, None) == ALIGN            # crow: 4-byte aligned
+    assert fl(A, 64, 96, A, A, A, None) == SHAPE
+    assert fl(None, 0, 64, None, None, None, None) == OK  # no block rows: nothing to do
+    assert fl(None, 64, 64, A, A, A, None) == NULL
+    assert fl(A, 64, 64, A, A + 1, A, None) == ALIGN
+    assert fl(A, 64, 64, A, A, U, None) == ALIGN
+    assert li(A, 4, 128, A, A, A, 64, None, A, 2, None) == DTYPE
+    assert li(A, 4, 96, A, A, A, 64, None, A, 0, None) == SHAPE      # k % 64
+    assert li(A, 4, 128, A, A, A, 80, None, A, 0, None) == SHAPE     # n % 64
+    assert li(A, -1, 128, A, A, A, 64, None, A, 0, None) == SHAPE
+    assert li(None, 0, 128, None, None, None, 64, None, None, 0, None) == OK   # empty
+    assert li(A, 4, 128, A, A, A, 0, None, A, 0, None) == OK
+    assert li(None, 4, 128, A, A, A, 64, None, A, 0, None) == NULL
+    assert li(A, 4, 128, None, A, A, 64, None, A, 0, None) == NULL
+    assert li(A, 4, 128, A, A, A, 64, None, None, 1, None) == NULL
+    assert li(U, 4, 128, A, A, A, 64, None, A, 0, None) == ALIGN
+    assert li(A, 4, 128, A, A, A, 64, U, A, 0, None) == ALIGN        # bias
+    assert li(A, 4, 128, A, A + 2, A, 64, None, A, 0, None) == ALIGN  # col
