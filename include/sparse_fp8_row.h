@@ -212,11 +212,10 @@ sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const flo
  * quantized dynamically, per call).  xq and xs receive exactly the bytes
  * quantize_rowwise_fp8 writes; out is as sparse_fp8_scaled_linear.
  *
- * For the smallest decode shapes -- k 2048 or 4096 and m * k <= 4096 -- both
- * steps run in ONE launch: every workgroup quantizes the activation itself
- * into its on-chip operand stage (no workgroup waits for another).  Other
- * shapes take two launches (quantization, then the linear layer), which is
- * faster once the activation is larger.
+ * For one activation row (m == 1) with k a multiple of 1024 up to 16384,
+ * both steps run in ONE launch: every workgroup quantizes the row itself (no
+ * workgroup waits for another).  Other shapes take two launches
+ * (quantization, then the linear layer).
  *
  *   x      [m, k] bf16 bits, device, read.
  *   xq     [m, k] FP8 bytes (format x_dt), device, written.

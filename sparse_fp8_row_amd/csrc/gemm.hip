@@ -672,6 +672,24 @@ __device__ __forceinline__ void row_bcast_steps(v8i (&b)[8], const v4i& x, std::
   ((b[S] = row_bcast_pair<S>(x)), ...);
 }
 
+// One unit's 8 MFMA steps for a single activation row: step S's operand is
+// broadcast from x1 (row_bcast_pair<S>) just before its MFMA, so only one
+// step's operand is live at a time.
+template <int XF, int WF, int S>
+__device__ __forceinline__ void x1_step(v4f& acc0, v4f& acc1, const v4i& x1, const uint8_t* region, uint32_t a_even,
+                                        uint32_t a_odd, uint32_t i_row, int r7) {
+  const v4i a = *reinterpret_cast<const v4i*>(region + ((S & 1) ? a_odd : a_even) + 128 * (S >> 1));
+  const int idx = *reinterpret_cast<const int*>(region + i_row + 16 * (S ^ r7));
+  const v8i b = row_bcast_pair<S>(x1);
+  if constexpr (S & 1) acc1 = smfmac16<XF, WF>(a, b, acc1, idx);
+  else acc0 = smfmac16<XF, WF>(a, b, acc0, idx);
+}
+template <int XF, int WF, int... S>
+__device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, const uint8_t* region, uint32_t a_even,
+                                        uint32_t a_odd, uint32_t i_row, int r7, std::integer_sequence<int, S...>) {
+  (x1_step<XF, WF, S>(acc0, acc1, x1, region, a_even, a_odd, i_row, r7), ...);
+}
+
 // Decode kernel, one k unit per wavefront.  A workgroup owns RT * 16 weight
 // rows and K / 1024 "units" of 1024 k (8 MFMA steps) each; wavefront w takes
 // units w, w + NW, ...  For a unit it puts the unit's compressed values
@@ -811,217 +829,6 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode with the activation quantization fused in (small M * K).
-// ---------------------------------------------------------------------------
-// One launch does both steps of the layer.  Every workgroup owns 16 weight
-// rows and first puts the loads of its whole weight block into LDS in flight.  While they stream, it quantizes the whole
-// (small) activation itself, exactly as quantize_rowwise_fp8 does: row maxima
-// of the bf16 magnitude bits by LDS atomic max (an exact, order-free maximum),
-// then scale, reciprocal and cast8 per 8 elements, the codes written straight
-// into an LDS activation stage (each 16-byte chunk of a row at
-// chunk ^ (row & 7), as the weight block) and the row scales into LDS for the
-// epilogue.  Workgroup 0 also
-// writes the codes and scales to xq / xs.  No workgroup waits for another.
-// The redundant quantization costs about 20 ALU operations per element in
-// every workgroup, and its first LDS access waits for the weight block (the
-// compiler cannot separate the two LDS regions' accesses), so the fused path
-// pays only for a tiny activation: measured at K = 4096, 6.5 us against 8.3 us
-// for two launches at M = 1, but 14.2 us against 9.0 us at M = 4.  It is used
-// while M * K <= 4096.
-constexpr int kFusedThreads = 256;
-constexpr int kFusedMaxElems = 4096;  // M * K
-constexpr int kFusedCPT = kFusedMaxElems / 8 / kFusedThreads;  // 8-element chunks per thread
-
-// KT = K / 128 is a template parameter (a multiple of 16) so that the weight
-// loads unroll to a known count and waiting for the activation registers
-// leaves them in flight.
-template <int XF, int WF, int OUT, int KT>
-__global__ __launch_bounds__(kFusedThreads) void linear_decode_fused_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
-    const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const float* __restrict__ ws,
-    const uint16_t* __restrict__ bias, void* __restrict__ out, int M, int N, int ws_stride) {
-  static_assert(KT % 16 == 0, "whole metadata loads per wavefront");
-  constexpr int K = KT * KSTEP;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // weight block
-  // The activation's LDS is separate from the weight block's, so the compiler
-  // can tell that writing it need not wait for the weight loads in flight.
-  __shared__ __attribute__((aligned(16))) uint8_t xcodes[kFusedMaxElems];
-  __shared__ uint32_t rmax[16];
-  __shared__ float rscale[16];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  constexpr int vbytes = 16 * (K / 2), mbytes = 16 * (K / 8);
-  const uint8_t* vblk = values + (int64_t)n0 * (K / 2);
-  const uint8_t* mblk = meta + (int64_t)n0 * (K / 8);
-  const int vchunks_row = K / 32, mchunks_row = K / 128;
-  constexpr int xchunks_row = K / 16;
-
-  // 1. epilogue operands that do not depend on the activation, the activation
-  // chunks into registers, then the weight block into LDS.  In this order,
-  // waiting for the activation (vmcnt counts in issue order) leaves the weight
-  // loads in flight.
-  const int m = r16, n = n0 + 4 * lg;
-  v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
-  uint2 b2 = make_uint2(0, 0);
-  if (wave == 0) {
-    w4 = load_ws4(ws, n, ws_stride);
-    if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
-  }
-  const int rchunks = K / 8, nchunks = M * rchunks;
-  const uint4* xv = reinterpret_cast<const uint4*>(x);
-  uint4 buf[kFusedCPT];
-#pragma unroll
-  for (int i = 0; i < kFusedCPT; ++i) {
-    const int t = min(tid + kFusedThreads * i, nchunks - 1);  // in bounds; extra chunks unused
-    buf[i] = xv[t];
-  }
-#pragma unroll
-  for (int j = 0; j < vbytes / 1024 / 4; ++j) {
-    const int q = wave + 4 * j;
-    const int p = q * 64 + lane, row = p / vchunks_row;
-    __builtin_amdgcn_global_load_lds((void*)(vblk + 16 * (p ^ (row & 7))), (void*)(smem + q * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < mbytes / 1024 / 4; ++j) {
-    const int q = wave + 4 * j;
-    const int p = q * 64 + lane, row = p / mchunks_row;
-    __builtin_amdgcn_global_load_lds((void*)(mblk + 16 * (p ^ (row & 7))), (void*)(smem + vbytes + q * 1024), 16, 0,
-                                     0);
-  }
-
-  // 2. row maxima (barriers that wait only for LDS operations, not for the
-  // weight stream)
-  if (tid < 16) rmax[tid] = 0;
-  lds_barrier();
-  // The 64 chunks a wavefront holds in slot i lie in one row (a row is a
-  // multiple of 64 chunks), so a wavefront maximum and one atomic per slot.
-#pragma unroll
-  for (int i = 0; i < kFusedCPT; ++i) {
-    const int t0 = wave * 64 + kFusedThreads * i;  // the wavefront's first chunk in slot i
-    if (t0 < nchunks) {
-      const uint32_t mw = wave_max(mag_max8(buf[i], 0u));
-      if (lane == 0) __hip_atomic_fetch_max(rmax + t0 / rchunks, mw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
-  lds_barrier();
-
-  // 3. cast: codes into the LDS activation stage (and, in workgroup 0, to xq)
-  const bool out0 = blockIdx.x == 0;
-#pragma unroll
-  for (int i = 0; i < kFusedCPT; ++i) {
-    const int t = tid + kFusedThreads * i;
-    if (t < nchunks) {
-      const int row = t / rchunks, c = t - row * rchunks;
-      const uint32_t mm = rmax[row];
-      const float sc = bf16_to_f32(mm) / Fp8<XF>::fmax;
-      const float rc = 1.0f / sc;
-      const uint2 v = mm == 0 ? zero8(buf[i]) : cast8<XF>(buf[i], sc, rc);
-      const int g = row * xchunks_row + (c >> 1);  // 16-byte chunk of the row-major codes
-      *reinterpret_cast<uint2*>(xcodes + 16 * (g ^ (row & 7)) + 8 * (c & 1)) = v;
-      if (out0) reinterpret_cast<uint2*>(xq)[t] = v;
-      if (c == 0) {
-        rscale[row] = mm == 0 ? 0.0f : sc;
-        if (out0) xs[row] = mm == 0 ? 0.0f : sc;
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // weight block landed, codes written
-  stage_barrier();
-  const float xsm = rscale[min(m, M - 1)];
-
-  // 4. MFMAs over this wavefront's quarter of the k steps, operands from LDS
-  const int s_lo = (KT * wave) / 4, s_hi = (KT * (wave + 1)) / 4;
-  const bool xon = r16 < M;
-  const v4i z4 = v4i{0, 0, 0, 0};
-  const int xr = min(r16, M - 1);
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f}, acc2 = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = s_lo; s0 < s_hi; s0 += 4) {
-    v4i a[4], lo[4], hi[4];
-    int idx[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = min(s0 + u, s_hi - 1);
-      const int pv = r16 * vchunks_row + 4 * s + lg;
-      const int pm = r16 * mchunks_row + s;
-      const int px = xr * xchunks_row + 8 * s + lg;
-      a[u] = *reinterpret_cast<const v4i*>(smem + 16 * (pv ^ (r16 & 7)));
-      idx[u] = *reinterpret_cast<const int*>(smem + vbytes + 16 * (pm ^ (r16 & 7)) + 4 * lg);
-      lo[u] = *reinterpret_cast<const v4i*>(xcodes + 16 * (px ^ (xr & 7)));
-      hi[u] = *reinterpret_cast<const v4i*>(xcodes + 16 * ((px + 4) ^ (xr & 7)));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool live = s0 + u < s_hi;
-      const v4i av = live ? a[u] : z4;
-      const v4i l = xon ? lo[u] : z4, h = xon ? hi[u] : z4;
-      const v8i b = v8i{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
-      if (u & 1) acc2 = smfmac16<XF, WF>(av, b, acc2, idx[u]);
-      else acc = smfmac16<XF, WF>(av, b, acc, idx[u]);
-    }
-  }
-  acc += acc2;
-
-  // 5. fixed-order reduction of the 4 partial tiles, epilogue
-  stage_barrier();
-  v4f* redv = reinterpret_cast<v4f*>(smem);
-  redv[wave * 64 + lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    v4f t = redv[lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) t += redv[w * 64 + lane];
-    v4f y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
-    if (bias) {
-      y[0] += bf16_to_f32(b2.x & 0xFFFFu);
-      y[1] += bf16_to_f32(b2.x >> 16);
-      y[2] += bf16_to_f32(b2.y & 0xFFFFu);
-      y[3] += bf16_to_f32(b2.y >> 16);
-    }
-    if (m < M) store4<OUT>(out, N, m, n, y);
-  }
-}
-
-// LDS bytes of the fused decode kernel, or 0 when the shape does not take it.
-// Dynamic LDS (the weight block) of the fused decode kernel, or 0 when the
-// shape does not take it; the kernel's static LDS holds the activation.
-// The static arrays take about 5 KB; 20 KB are left to them.
-constexpr int64_t kFusedMaxDynLds = 140 * 1024;
-inline int64_t fused_decode_lds(int64_t m, int64_t k) {
-  if (m < 1 || m > 16 || m * k > kFusedMaxElems) return 0;
-  if (k != 2048 && k != 4096) return 0;
-  const int64_t bytes = 10 * k;  // values + metadata of 16 rows
-  return bytes <= kFusedMaxDynLds ? bytes : 0;
-}
-
-template <int XF, int WF, int OUT, int KT>
-hipError_t run_decode_fused_kt(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
-  const int64_t lds = fused_decode_lds(a.m, a.k);
-  auto kern = linear_decode_fused_kernel<XF, WF, OUT, KT>;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxDynLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(kFusedThreads), (unsigned)lds, stream, x, xq, xs,
-                     a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, a.ws_stride);
-  return hipGetLastError();
-}
-
-template <int XF, int WF, int OUT>
-hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
-  switch (a.k) {
-    case 2048: return run_decode_fused_kt<XF, WF, OUT, 16>(x, xq, xs, a, stream);
-    default: return run_decode_fused_kt<XF, WF, OUT, 32>(x, xq, xs, a, stream);  // 4096
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Kernel configurations ("algorithms") and the default choice by shape
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
@@ -1074,6 +881,188 @@ template <int XF, int WF, int OUT, int RT>
 hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
   if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, RT, true>(a, stream);
   return run_decode_unit_cfg<XF, WF, OUT, RT, false>(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode from the bf16 activation, one row: quantization fused in front of
+// the unit kernel.
+// ---------------------------------------------------------------------------
+// The single-row form of linear_decode_unit_kernel (same units, LDS regions,
+// row broadcast of the activation and reduction) that first quantizes the
+// bf16 row itself, exactly as quantize_rowwise_fp8 does.  Every wavefront
+// starts its first unit's weight loads, then loads the bf16 values of its
+// units that its lanes will hold as codes (lane (r, g): the 16 elements
+// 8 (r >> 1) + 4 (r & 1) + g of a unit, in 16-byte chunks of codes).  The
+// compiler makes the first use of those values wait for the weight loads as
+// well (ordinary and global->LDS loads pending together count as unordered,
+// and any LDS access waits for pending global->LDS loads), so the row
+// maximum (over lanes by DPP, over wavefronts through LDS; every wavefront
+// reading the whole row instead measured slower), the scale, its reciprocal
+// and cast8 run once the weight block has landed: a few hundred cycles after
+// the stream, against a second launch.  Workgroup 0 also
+// writes the codes and the scale to xq / xs.  A wavefront holds at most 2
+// units of the activation (K <= 16384 with 8 wavefronts).
+constexpr int kFusedMaxUnitsPerWave = 2;
+
+// Wavefront maximum without LDS-path instructions (DPP row shifts, readlane).
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t m) {
+  // row_shr 1, 2, 4, 8 (DPP controls 0x111 .. 0x118; lanes shifted in from
+  // outside the 16-lane row read 0): lane 15 of each row ends with the row's
+  // maximum
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+  return max(max(a, b), max(c, d));
+}
+
+template <int XF, int WF, int OUT, int NWMAX>
+__global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_unit_fused1_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
+    const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const float* __restrict__ ws,
+    const uint16_t* __restrict__ bias, void* __restrict__ out, int N, int K, int ws_stride) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NWMAX * kUnitLds];
+  __shared__ uint32_t wmax[NWMAX];  // static LDS sized for NWMAX wavefronts
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NW = blockDim.x / 64;
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int NU = K / kUnitK;
+  // this wavefront's units: 1, or 2 when there are more units than 8 wavefronts
+  constexpr int UPW = NWMAX == 8 ? kFusedMaxUnitsPerWave : 1;
+  const int nuw = (NU - wave + NW - 1) / NW;
+  uint8_t* region = smem + wave * kUnitLds;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int vrow_l = lane >> 5, vc = lane & 31, mrow_l = lane >> 3, mc = lane & 7;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(vrow_l * (K / 2) + 16 * (vc ^ ((2 * i + vrow_l) & 7)));
+  const uint32_t moff = (uint32_t)(mrow_l * (K / 8) + 16 * (mc ^ (mrow_l & 7)));
+  const int r7 = r16 & 7;
+  const uint32_t a_even = r16 * 512 + 16 * ((4 * ((r7 >> 2) & 1)) | (lg ^ (r7 & 3)));
+  const uint32_t a_odd = r16 * 512 + 16 * ((4 * (((r7 >> 2) & 1) ^ 1)) | (lg ^ (r7 & 3)));
+  const uint32_t i_row = 8192 + r16 * 128 + 4 * lg;
+  // this lane's 16 activation elements of a unit (and its 16 code bytes)
+  const int xoff = 128 * (r16 >> 1) + 64 * (r16 & 1) + 16 * lg;
+
+  auto dma = [&](int u0) __attribute__((always_inline)) {
+    const uint8_t* vu = values + n0 * (K / 2) + u0 * (kUnitK / 2);
+    const uint8_t* mu = meta + n0 * (K / 8) + u0 * (kUnitK / 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((void*)(vu + (int64_t)i * K + voff[i & 3]), (void*)(region + i * 1024), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds((void*)(mu + (int64_t)i * K + moff), (void*)(region + 8192 + i * 1024), 16, 0,
+                                       0);
+  };
+
+  // 1. epilogue operands, the activation of this wavefront's units, then the
+  // first unit's weight loads
+  const int n = (int)n0 + 4 * lg;
+  v4f w4 = v4f{0.f, 0.f, 0.f, 0.f};
+  uint2 b2 = make_uint2(0, 0);
+  if (wave == 0) {
+    w4 = load_ws4(ws, n, ws_stride);
+    if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
+  }
+  dma(wave);
+  uint4 xa[UPW][2];
+#pragma unroll
+  for (int c = 0; c < UPW; ++c) {
+    const int u0 = wave + c * NW;
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (int64_t)min(u0, NU - 1) * kUnitK + xoff);
+    xa[c][0] = xp[0];
+    xa[c][1] = xp[1];
+  }
+
+  // 2. row maximum over lanes, then wavefronts
+  uint32_t mx = 0;
+#pragma unroll
+  for (int c = 0; c < UPW; ++c)
+    if (c < nuw) mx = mag_max8(xa[c][1], mag_max8(xa[c][0], mx));
+  mx = wave_max_dpp(mx);
+  if (lane == 0) wmax[wave] = mx;
+  lds_barrier();
+  uint32_t mm = wmax[0];
+  for (int w = 1; w < NW; ++w) mm = max(mm, wmax[w]);
+  const float sc = bf16_to_f32(mm) / Fp8<XF>::fmax;
+  const float rc = 1.0f / sc;
+
+  // 3. codes of this wavefront's units (workgroup 0 also stores them)
+  v4i x1[UPW];
+  const bool out0 = blockIdx.x == 0;
+#pragma unroll
+  for (int c = 0; c < UPW; ++c) {
+    if (c < nuw) {
+      const uint2 lo = mm == 0 ? zero8(xa[c][0]) : cast8<XF>(xa[c][0], sc, rc);
+      const uint2 hi = mm == 0 ? zero8(xa[c][1]) : cast8<XF>(xa[c][1], sc, rc);
+      x1[c] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      if (out0) *reinterpret_cast<v4i*>(xq + (int64_t)(wave + c * NW) * kUnitK + xoff) = x1[c];
+    }
+  }
+  const float xsm = mm == 0 ? 0.0f : sc;
+  if (out0 && tid == 0) xs[0] = xsm;
+
+  // 4. the units: weight block in LDS, the codes broadcast per step, MFMAs
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+  for (int c = 0; c < UPW; ++c) {
+    if (c < nuw) {
+      if (c > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // the previous unit's LDS reads are done
+        dma(wave + c * NW);
+      }
+      wait_vmcnt<0>();
+      x1_unit<XF, WF>(acc0, acc1, x1[c], region, a_even, a_odd, i_row, r7, std::make_integer_sequence<int, 8>{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  // 5. fixed-order reduction of the partial tiles, epilogue
+  reinterpret_cast<v4f*>(region)[lane] = acc0 + acc1;
+  __syncthreads();
+  if (wave == 0) {
+    v4f t = reinterpret_cast<const v4f*>(smem)[lane];
+    for (int w = 1; w < NW; ++w) t += reinterpret_cast<const v4f*>(smem + w * kUnitLds)[lane];
+    v4f y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = t[i] * (xsm * w4[i]);
+    if (bias) {
+      y[0] += bf16_to_f32(b2.x & 0xFFFFu);
+      y[1] += bf16_to_f32(b2.x >> 16);
+      y[2] += bf16_to_f32(b2.y & 0xFFFFu);
+      y[3] += bf16_to_f32(b2.y >> 16);
+    }
+    if (r16 == 0) store4<OUT>(out, N, 0, n, y);
+  }
+}
+
+// Fused path of the bf16-activation entry point: one activation row,
+// K a multiple of 1024 up to 16384.
+inline bool fused_decode_ok(int64_t m, int64_t k) {
+  return m == 1 && k % kUnitK == 0 && k <= 8 * kFusedMaxUnitsPerWave * kUnitK;
+}
+
+template <int XF, int WF, int OUT, int NWMAX>
+hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int nw,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL((linear_decode_unit_fused1_kernel<XF, WF, OUT, NWMAX>), dim3((unsigned)(a.n / 16)),
+                     dim3(64 * nw), 0, stream, x, xq, xs, a.values, a.meta, a.ws, a.bias, a.out, (int)a.n, (int)a.k,
+                     a.ws_stride);
+  return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT>
+hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
+  // the static LDS is sized for the smallest of 2, 4, 8 wavefronts that covers
+  // the units, so small K keeps several workgroups per CU
+  const int nw = unit_waves(a.k);
+  if (nw <= 2) return run_decode_fused_nw<XF, WF, OUT, 2>(x, xq, xs, a, nw, stream);
+  if (nw <= 4) return run_decode_fused_nw<XF, WF, OUT, 4>(x, xq, xs, a, nw, stream);
+  return run_decode_fused_nw<XF, WF, OUT, 8>(x, xq, xs, a, nw, stream);
 }
 
 template <int XF, int WF, int OUT>
@@ -1170,7 +1159,7 @@ hipError_t run_fused_out(const uint16_t* x, uint8_t* xq, float* xs, const Linear
 
 hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a,
                                  hipStream_t stream) {
-  if (fused_decode_lds(a.m, a.k) == 0) {
+  if (!fused_decode_ok(a.m, a.k)) {
     // two launches: the row-wise quantization, then the linear layer
     hipError_t e = launch_quantize(x, a.m, a.k, a.x_fmt, xq, xs, stream);
     if (e != hipSuccess) return e;

@@ -1,11 +1,12 @@
 """GPU parity of sparse_fp8_rowwise_linear_dynamic (activation quantization
-fused into the decode GEMM launch).
+fused into the decode GEMM launch for one activation row).
 
 The codes and scales it writes are compared bit for bit with the oracle's
 row-wise quantization, the output with the oracle's linear layer (same rules
-as the row-wise tests), on every fused shape class (each supported K, M up
-to M*K = 16384, grids smaller and larger than the chip holds at once, row
-and tensor weight scales) and on shapes that take the two-launch path.
+as the row-wise tests), on every fused shape class (K from one 1024-k unit
+to 16384, one and two units per wavefront, uneven unit counts, grids smaller
+and larger than the chip holds at once, row and tensor weight scales, an
+all-zero row) and on shapes that take the two-launch path.
 """
 import sys
 
@@ -64,24 +65,43 @@ def run_case(gpu, case, wscale="row", seed_shift=0):
         assert r["strict_rate_ok"], r
 
 
-# (m, n, k): fused shapes (n/16 workgroups: 16 .. 896, more than the chip's 256 CUs)
-FUSED = [(1, 4096, 4096), (2, 1040, 2048), (1, 14336, 4096), (1, 256, 2048), (2, 6144, 2048)]
+# (m, n, k): fused shapes (n/16 workgroups: 16 .. 896, more than the chip's 256 CUs;
+# K/1024 units over up to 8 wavefronts: 1, 2, 4, 5 x (2,2,2,2,1), 7 x 2, 8 x 2)
+FUSED = [(1, 4096, 4096), (1, 1040, 1024), (1, 14336, 4096), (1, 256, 2048), (1, 2048, 9216), (1, 512, 14336),
+         (1, 4096, 16384)]
 
 
 @pytest.mark.parametrize("shape", FUSED, ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
 def test_dynamic_fused(gpu, shape):
     m, n, k = shape
     xf, wf = [(E4, E4), (E5, E4), (E4, E5), (E5, E5)][(m + n // 16) % 4]
-    run_case(gpu, sfr_inputs.Case(f"dyn_M{m}N{n}K{k}", 10, m, n, k, x_fmt=xf, w_fmt=wf, bias=(m % 2 == 0)))
+    run_case(gpu, sfr_inputs.Case(f"dyn_M{m}N{n}K{k}", 10, m, n, k, x_fmt=xf, w_fmt=wf, bias=((n // 16) % 2 == 0)))
 
 
 def test_dynamic_fused_tensor_weight_scale(gpu):
-    run_case(gpu, sfr_inputs.Case("dyn_tensor", 10, 2, 4096, 2048, x_fmt=E4, w_fmt=E5, bias=True), wscale="tensor")
+    run_case(gpu, sfr_inputs.Case("dyn_tensor", 10, 1, 4096, 2048, x_fmt=E4, w_fmt=E5, bias=True), wscale="tensor")
+    run_case(gpu, sfr_inputs.Case("dyn_tensor", 10, 2, 4096, 2048, x_fmt=E5, w_fmt=E5, bias=True), wscale="tensor")
 
 
-# shapes that take the two-launch path: m > 16, m*k > 16384, an unsupported k
+def test_dynamic_fused_zero_row(gpu):
+    # an all-zero activation row (both zero signs): codes keep each sign, scale 0, out = bias
+    n, k = 1024, 2048
+    case = sfr_inputs.Case("dyn_zero", 13, 1, n, k, bias=True)
+    xb = np.zeros((1, k), np.uint16)
+    xb[0, 1::3] = 0x8000
+    pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)), torch.float8_e4m3fn)
+    bb = sfr_inputs.draw_bias(case)
+    y, xq, xs = gpu.sparse_fp8_rowwise_linear_dynamic(dev_bf16(xb), pw.values, pw.meta, pw.scale, dev_bf16(bb))
+    torch.cuda.synchronize()
+    oxq, oxs = oracle.quantize_rows(xb, E4)
+    assert np.array_equal(host_bytes(xq), oxq)
+    assert host_f32(xs)[0] == 0.0 and oxs[0] == 0.0
+    assert np.array_equal(host_bf16_bits(y)[0], bb)
+
+
+# shapes that take the two-launch path: m > 1, k not a multiple of 1024, k > 16384
 @pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 4096, 14336), (16, 4096, 4096),
-                                   (2, 1024, 1024), (4, 4096, 4096), (1, 4096, 14336)],
+                                   (2, 1024, 1024), (4, 4096, 4096), (1, 4096, 640), (1, 256, 17408)],
                          ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
 def test_dynamic_two_launch(gpu, shape):
     m, n, k = shape
