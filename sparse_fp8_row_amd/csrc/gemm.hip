@@ -904,6 +904,38 @@ hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
 // units of the activation (K <= 16384 with 8 wavefronts).
 constexpr int kFusedMaxUnitsPerWave = 2;
 
+// First loads of the fused decode kernel: the wavefront's activation chunks
+// (global -> LDS into xl), then its first unit's weight block (into wl), a
+// wait until only the weight loads are pending, and the activation chunks
+// read back.  xl and wl are restrict parameters of an inlined function, so
+// the compiler can tell the activation reads from the pending weight loads
+// and does not make them wait for the whole stream.
+template <int UPW>
+__device__ __forceinline__ void fused_first_loads(uint8_t* __restrict__ xl, uint8_t* __restrict__ wl,
+                                                  const uint16_t* __restrict__ x, const uint8_t* vu, const uint8_t* mu,
+                                                  const uint32_t (&voff)[4], uint32_t moff, int K, int NU, int wave,
+                                                  int NW, int xoff, int lane, uint4 (&xa)[UPW][2]) {
+#pragma unroll
+  for (int c = 0; c < UPW; ++c) {
+    const int u0 = min(wave + c * NW, NU - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_global_load_lds((void*)(x + (int64_t)u0 * kUnitK + xoff + 8 * h), (void*)(xl + (2 * c + h) * 1024),
+                                       16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds((void*)(vu + (int64_t)i * K + voff[i & 3]), (void*)(wl + i * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds((void*)(mu + (int64_t)i * K + moff), (void*)(wl + 8192 + i * 1024), 16, 0, 0);
+  wait_vmcnt<10>();
+#pragma unroll
+  for (int c = 0; c < UPW; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xa[c][h] = reinterpret_cast<const uint4*>(xl + (2 * c + h) * 1024)[lane];
+}
+
 // Wavefront maximum without LDS-path instructions (DPP row shifts, readlane).
 __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t m) {
   // row_shr 1, 2, 4, 8 (DPP controls 0x111 .. 0x118; lanes shifted in from
@@ -923,8 +955,12 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
     const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const float* __restrict__ ws,
     const uint16_t* __restrict__ bias, void* __restrict__ out, int N, int K, int ws_stride) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NWMAX * kUnitLds];
-  __shared__ uint32_t wmax[NWMAX];  // static LDS sized for NWMAX wavefronts
+  // dynamic LDS: the weight regions, then the activation chunks, then the
+  // wavefront maxima
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  constexpr int UPW0 = NWMAX == 8 ? kFusedMaxUnitsPerWave : 1;
+  uint8_t* xbase = smem + NWMAX * kUnitLds;
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(xbase + NWMAX * UPW0 * 2048);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NW = blockDim.x / 64;
@@ -969,15 +1005,13 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
     w4 = load_ws4(ws, n, ws_stride);
     if (bias) b2 = *reinterpret_cast<const uint2*>(bias + n);
   }
-  dma(wave);
+  // the activation chunks by global->LDS loads too (lane l's 16 bytes at
+  // 16 l of each 1 KB), issued before the weight loads: all pending loads are
+  // then of one kind and complete in issue order, so once at most the weight
+  // loads are pending (vmcnt(10)) the activation has landed
   uint4 xa[UPW][2];
-#pragma unroll
-  for (int c = 0; c < UPW; ++c) {
-    const int u0 = wave + c * NW;
-    const uint4* xp = reinterpret_cast<const uint4*>(x + (int64_t)min(u0, NU - 1) * kUnitK + xoff);
-    xa[c][0] = xp[0];
-    xa[c][1] = xp[1];
-  }
+  fused_first_loads<UPW>(xbase + wave * UPW0 * 2048, region, x, values + n0 * (K / 2) + wave * (kUnitK / 2),
+                         meta + n0 * (K / 8) + wave * (kUnitK / 8), voff, moff, K, NU, wave, NW, xoff, lane, xa);
 
   // 2. row maximum over lanes, then wavefronts
   uint32_t mx = 0;
@@ -1049,9 +1083,17 @@ inline bool fused_decode_ok(int64_t m, int64_t k) {
 template <int XF, int WF, int OUT, int NWMAX>
 hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int nw,
                                hipStream_t stream) {
-  hipLaunchKernelGGL((linear_decode_unit_fused1_kernel<XF, WF, OUT, NWMAX>), dim3((unsigned)(a.n / 16)),
-                     dim3(64 * nw), 0, stream, x, xq, xs, a.values, a.meta, a.ws, a.bias, a.out, (int)a.n, (int)a.k,
-                     a.ws_stride);
+  constexpr unsigned lds = NWMAX * kUnitLds + NWMAX * (NWMAX == 8 ? kFusedMaxUnitsPerWave : 1) * 2048 + 4 * NWMAX;
+  auto kern = linear_decode_unit_fused1_kernel<XF, WF, OUT, NWMAX>;
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(64 * nw), lds, stream, x, xq, xs, a.values, a.meta, a.ws,
+                     a.bias, a.out, (int)a.n, (int)a.k, a.ws_stride);
   return hipGetLastError();
 }
 
