@@ -114,6 +114,68 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float
   }
 }
 
+// bf16 epilogue through LDS.  The accumulator layout gives each store
+// instruction 16 rows x 32 bytes, and output written that way reached about
+// half of what plain full-line writes reach (3.6 against 7 TB/s), which made
+// the stores of the 256 x 256 kernel a fifth of its time.  So a wavefront
+// writes its finished FN x FM block, scaled and rounded, row-major into
+// `region` (FM * 16 rows of FN * 32 bytes, each 16-byte chunk at
+// chunk ^ (row % chunks-per-row) so the writes and the reads spread over the
+// banks), and reads it back so that consecutive lanes hold consecutive
+// 16-byte chunks of a row: every store instruction then writes whole rows
+// of the tile (whole cache lines when a row is 128 bytes or more).  The
+// caller makes the LDS free first (every wavefront done with its last
+// stage); each wavefront uses only its own region.
+template <int FN, int FM>
+__device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[FN][FM], const float* __restrict__ xs,
+                                                    const float* __restrict__ ws, const uint16_t* __restrict__ bias,
+                                                    uint16_t* __restrict__ out, int M, int N, int mb, int nb, int r16,
+                                                    int lg, int lane, int xs_stride, int ws_stride, uint8_t* region) {
+  constexpr int CPR = FN * 2;               // 16-byte chunks per row (8 outputs each)
+  constexpr int ROWS = FM * 16, RPI = 64 / CPR;  // rows, rows per 64-lane pass
+  static_assert((CPR & (CPR - 1)) == 0 && CPR <= 64, "chunks per row");
+  float xsv[FM];
+  v4f wsv[FN];
+  uint2 bv[FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) xsv[fm] = xs[min(mb + fm * 16 + r16, M - 1) * xs_stride];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int nc = min(nb + fn * 16 + 4 * lg, N - 4);
+    wsv[fn] = load_ws4(ws, nc, ws_stride);
+    bv[fn] = bias ? *reinterpret_cast<const uint2*>(bias + nc) : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = fm * 16 + r16;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      v4f y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = acc[fn][fm][i] * (xsv[fm] * wsv[fn][i]);
+      if (bias) {
+        y[0] += bf16_to_f32(bv[fn].x & 0xFFFFu);
+        y[1] += bf16_to_f32(bv[fn].x >> 16);
+        y[2] += bf16_to_f32(bv[fn].y & 0xFFFFu);
+        y[3] += bf16_to_f32(bv[fn].y >> 16);
+      }
+      const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+      // outputs n = 16 fn + 4 lg .. + 3: chunk 2 fn + lg / 2, half lg % 2
+      const int c = (2 * fn + (lg >> 1)) ^ (row & (CPR - 1));
+      *reinterpret_cast<uint2*>(region + row * (CPR * 16) + c * 16 + 8 * (lg & 1)) = make_uint2(lo, hi);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes are done
+#pragma unroll
+  for (int t = 0; t < ROWS / RPI; ++t) {
+    const int row = t * RPI + lane / CPR, c = lane % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(region + row * (CPR * 16) + 16 * (c ^ (row & (CPR - 1))));
+    const int m = mb + row, n = nb + 8 * c;
+    if (m < M && n < N) *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiled kernel
 // ---------------------------------------------------------------------------
@@ -158,7 +220,8 @@ struct Tiled {
   static constexpr int FN = TN / 16, FM = TM / 16;  // 16x16 blocks per wavefront
   static constexpr int W_BYTES = BN * 64, META_BYTES = BN * 16, X_BYTES = BM * 128;
   static constexpr int STAGE = W_BYTES + META_BYTES + X_BYTES;
-  static constexpr int LDS = S * STAGE;
+  static constexpr int EPI = NW * FN * FM * 512;  // bf16 epilogue staging (store_tile_bf16_lds)
+  static constexpr int LDS = S * STAGE > EPI ? S * STAGE : EPI;
   static_assert(BN % 64 == 0 && BM % 8 == 0, "tile");
   static_assert(BN % (16 * WN) == 0 && BM % (16 * WM) == 0, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -354,8 +417,16 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     }
   }
 
-  // ---- epilogue: scales, bias, bf16, store ----
-  store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
+  // ---- epilogue: scales, bias, bf16, store (bf16 through LDS, once every
+  // wavefront is done with the last stage) ----
+  if constexpr (OUT == OUT_BF16) {
+    lds_barrier();
+    store_tile_bf16_lds<C::FN, C::FM>(acc, xs, ws, bias, reinterpret_cast<uint16_t*>(out), M, N, m0 + wm * C::TM,
+                                      n0 + wn * C::TN, r16, lg, lane, xs_stride, ws_stride,
+                                      smem + wave * (C::FN * C::FM * 512));
+  } else {
+    store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -542,7 +613,13 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc_fence(acc[i][j]);
-    store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
+    if constexpr (OUT == OUT_BF16) {
+      lds_barrier();
+      store_tile_bf16_lds<FN, FM>(acc, xs, ws, bias, reinterpret_cast<uint16_t*>(out), M, N, m0 + wm * C::TM,
+                                  n0 + wn * C::TN, r16, lg, lane, xs_stride, ws_stride, smem + wave * (FN * FM * 512));
+    } else {
+      store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
+    }
   };
   if (KT & 1) steps(T1{});
   else steps(F0{});
