@@ -123,9 +123,10 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float
 // chunk ^ (row % chunks-per-row) so the writes and the reads spread over the
 // banks), and reads it back so that consecutive lanes hold consecutive
 // 16-byte chunks of a row: every store instruction then writes whole rows
-// of the tile (whole cache lines when a row is 128 bytes or more).  The
-// caller makes the LDS free first (every wavefront done with its last
-// stage); each wavefront uses only its own region.
+// of the tile (whole cache lines when a row is 128 bytes or more).  N is a
+// multiple of 16 (checked at the boundary), so a chunk that starts below N
+// lies wholly inside the row.  The caller makes the LDS free first (every
+// wavefront done with its last stage); each wavefront uses only its own region.
 template <int FN, int FM>
 __device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[FN][FM], const float* __restrict__ xs,
                                                     const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -213,19 +214,25 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int x_chunk(int row, int j) { return j ^ (row & 7); }
 __device__ __forceinline__ int w_chunk(int row, int j) { return j ^ ((row >> 1) & 3); }
 
-template <int BN, int BM, int WN, int WM, int S>
+// MB = 0: each stage holds its k step's metadata.  MB > 0: metadata moves in
+// blocks of MB k steps (16 * MB bytes of each weight row, whole 128-byte
+// lines for MB = 8) into two LDS buffers of their own after the stages.
+template <int BN, int BM, int WN, int WM, int S, int MB = 0>
 struct Tiled {
   static constexpr int NW = WN * WM, NT = 64 * NW;
   static constexpr int TN = BN / WN, TM = BM / WM;  // wavefront tile
   static constexpr int FN = TN / 16, FM = TM / 16;  // 16x16 blocks per wavefront
-  static constexpr int W_BYTES = BN * 64, META_BYTES = BN * 16, X_BYTES = BM * 128;
+  static constexpr int W_BYTES = BN * 64, META_BYTES = MB ? 0 : BN * 16, X_BYTES = BM * 128;
   static constexpr int STAGE = W_BYTES + META_BYTES + X_BYTES;
+  static constexpr int META_BLOCK = MB ? BN * 16 * MB : 0;  // one metadata block buffer
+  static constexpr int MAIN = S * STAGE + 2 * META_BLOCK;
   static constexpr int EPI = NW * FN * FM * 512;  // bf16 epilogue staging (store_tile_bf16_lds)
-  static constexpr int LDS = S * STAGE > EPI ? S * STAGE : EPI;
+  static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
   static_assert(BN % 64 == 0 && BM % 8 == 0, "tile");
   static_assert(BN % (16 * WN) == 0 && BM % (16 * WM) == 0, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(S >= 2, "stages");
+  static_assert(MB == 0 || (MB == 8 && S == 2 && BN % (8 * NW) == 0), "metadata blocks: 8 steps, two stages");
 };
 
 // Global -> LDS loader of one pipeline stage.  The stage is W_INSTR + M_INSTR
@@ -236,9 +243,9 @@ struct Tiled {
 // swizzles depend on row bits that one instruction's 16 or 8 rows do not
 // change), so only the row moves.  Rows past the matrix edge are clamped to
 // the last row (read, never stored).
-template <int BN, int BM, int NW>
+template <int BN, int BM, int NW, bool META = true>
 struct StageLoader {
-  static constexpr int W_INSTR = BN / 16, M_INSTR = BN / 64, X_INSTR = BM / 8;
+  static constexpr int W_INSTR = BN / 16, M_INSTR = META ? BN / 64 : 0, X_INSTR = BM / 8;
   static constexpr int W_PW = W_INSTR / NW, X_PW = X_INSTR / NW;
   static constexpr int M_PW = (M_INSTR + NW - 1) / NW;
   static constexpr int PER_WAVE_MIN = W_PW + X_PW + M_INSTR / NW;  // loads per stage, every wavefront
@@ -290,7 +297,7 @@ struct StageLoader {
       const uint8_t* g = values + (int64_t)min(w_row0 + 16 * j, n_last) * ldv + w_col + kb / 2;
       __builtin_amdgcn_global_load_lds((void*)g, (void*)(stage_base + (wave * W_PW + j) * 1024), 16, 0, 0);
     }
-    if (M_INSTR >= NW || wave < M_INSTR) {
+    if (M_INSTR > 0 && (M_INSTR >= NW || wave < M_INSTR)) {
 #pragma unroll
       for (int j = 0; j < M_PW; ++j) {
         const uint8_t* g = meta + (int64_t)min(m_row0 + 64 * NW * j, n_last) * ldm + kb / 8;
@@ -306,12 +313,12 @@ struct StageLoader {
   }
 };
 
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC, int MB>
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
-  using C = Tiled<BN, BM, WN, WM, S>;
+  using C = Tiled<BN, BM, WN, WM, S, MB>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // ---- tile assignment: contiguous runs per XCD, grouped along n ----
@@ -334,9 +341,30 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   const int64_t ldv = K / 2, ldm = K / 8, ldx = K;
 
   // ---- this wavefront's share of the per-stage loads (global -> LDS) ----
-  const StageLoader<BN, BM, C::NW> loader(values, meta, xq, K, N, M, n0, m0, wave, lane);
+  const StageLoader<BN, BM, C::NW, MB == 0> loader(values, meta, xq, K, N, M, n0, m0, wave, lane);
   auto issue = [&](int kt, int slot) { loader.issue(smem + slot * C::STAGE, kt); };
-  constexpr int LPW = StageLoader<BN, BM, C::NW>::PER_WAVE_MIN;
+  constexpr int LPW = StageLoader<BN, BM, C::NW, MB == 0>::PER_WAVE_MIN;
+  const int KT = K / KSTEP;
+
+  // ---- metadata blocks (MB > 0): block b = k steps MB b .. MB b + MB - 1,
+  // row r's 16-byte chunk of step s at chunk s ^ (r % 8) of the row's 16 MB
+  // bytes, in buffer b % 2.  One 1 KB load = 8 rows x 8 chunks; each
+  // wavefront loads BN / (8 NW) of them.  Chunks past the last k step repeat
+  // that step's chunk (loaded, never read). ----
+  uint8_t* const meta_lds = smem + S * C::STAGE;
+  auto issue_meta = [&](int blk) {
+    if constexpr (MB > 0) {
+      constexpr int PW = BN / (8 * C::NW);
+      const int s = min((lane & 7) ^ ((lane >> 3) & 7), KT - MB * blk - 1);
+#pragma unroll
+      for (int j = 0; j < PW; ++j) {
+        const int row = (wave * PW + j) * 8 + (lane >> 3);
+        const uint8_t* g = meta + (int64_t)min(n0 + row, N - 1) * ldm + 16 * (MB * blk + s);
+        __builtin_amdgcn_global_load_lds((void*)g, (void*)(meta_lds + (blk & 1) * C::META_BLOCK + (wave * PW + j) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
 
   // ---- LDS read offsets of this lane's MFMA operands ----
   int a_off[C::FN], i_off[C::FN], b_off0[C::FM], b_off1[C::FM];
@@ -344,7 +372,8 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   for (int f = 0; f < C::FN; ++f) {
     const int r = wn * C::TN + f * 16 + r16;
     a_off[f] = r * 64 + 16 * w_chunk(r, lg);
-    i_off[f] = C::W_BYTES + r * 16 + 4 * lg;
+    // MB > 0: offset from the stage base to the row's metadata (step chunk added per step)
+    i_off[f] = MB ? (int)(meta_lds - smem) + r * (16 * MB) + 4 * lg : C::W_BYTES + r * 16 + 4 * lg;
   }
 #pragma unroll
   for (int f = 0; f < C::FM; ++f) {
@@ -359,18 +388,27 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = K / KSTEP;
+  issue_meta(0);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < KT) issue(s, s);
 
   for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once at most the loads of the S-2 later stages are pending
+    // stage kt has landed once at most the loads of the S-2 later stages are
+    // pending (metadata blocks only with two stages: everything has landed)
     if (kt + S - 2 < KT) wait_vmcnt<LPW * (S - 2)>();
     else wait_vmcnt<0>();
     stage_barrier();
+    // block kt / MB + 1 goes to the buffer that block kt / MB - 1 used, free
+    // since every wavefront passed this barrier after its last step
+    if constexpr (MB > 0)
+      if (kt % MB == 0 && kt + MB < KT) issue_meta(kt / MB + 1);
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const uint8_t* base = smem + (kt % S) * C::STAGE;
+    // metadata of step kt relative to the stage base: chunk (kt % MB) ^ (row % 8), rows % 8 = r16 % 8
+    const int mo = MB ? 16 * ((kt % (MB ? MB : 1)) ^ (r16 & 7)) + ((kt / (MB ? MB : 1)) & 1) * C::META_BLOCK -
+                            (int)(base - smem)
+                      : 0;
     if constexpr (ORD == 0) {
       // all weight operands of the wavefront tile, then one activation block at
       // a time: each 32-byte B fragment feeds FN instructions
@@ -379,7 +417,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
         a[fn] = *reinterpret_cast<const v4i*>(base + a_off[fn]);
-        idx[fn] = *reinterpret_cast<const int*>(base + i_off[fn]);
+        idx[fn] = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
       }
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
@@ -401,12 +439,12 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
       v4i a[2];
       int idx[2];
       a[0] = *reinterpret_cast<const v4i*>(base + a_off[0]);
-      idx[0] = *reinterpret_cast<const int*>(base + i_off[0]);
+      idx[0] = *reinterpret_cast<const int*>(base + i_off[0] + mo);
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
         if (fn + 1 < C::FN) {
           a[(fn + 1) & 1] = *reinterpret_cast<const v4i*>(base + a_off[fn + 1]);
-          idx[(fn + 1) & 1] = *reinterpret_cast<const int*>(base + i_off[fn + 1]);
+          idx[(fn + 1) & 1] = *reinterpret_cast<const int*>(base + i_off[fn + 1] + mo);
         }
         if constexpr (ORD == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -911,13 +949,13 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1, int MB = 0>
 hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
-  using C = Tiled<BN, BM, WN, WM, S>;
+  using C = Tiled<BN, BM, WN, WM, S, MB>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC>;
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC, MB>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1208,7 +1246,7 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
     case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
     case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
-    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2>(a, stream);
+    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
   }
@@ -1255,7 +1293,7 @@ int linear_default_algo(int64_t m, int64_t n, int64_t k) {
   }
   const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = ((m + 127) / 128) * ((n + 127) / 128);
-  if (big >= 512) return k >= 48 * KSTEP ? ALGO_WIDE_256 : ALGO_TILED_256;
+  if (big >= 512) return ALGO_TILED_256;
   if (mid >= 256) return ALGO_TILED_128;
   return ALGO_TILED_64;
 }

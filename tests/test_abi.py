@@ -180,7 +180,7 @@ def test_linear_algos(lib):
     assert d(1, 4096, 4096) == 0 and d(16, 4096, 14336) == 0 and d(16, 4096, 17408) == 0
     assert d(1, 14336, 4096) == 0 and d(4, 14336, 4096) == 6 and d(16, 6144, 4096) == 6
     assert d(16, 6144, 640) == 1 and d(4, 6160, 4096) == 0
-    assert d(8192, 14336, 4096) == 4 and d(8192, 14336, 6144) == 5 and d(8192, 14336, 256) == 4
+    assert d(8192, 14336, 4096) == 4 and d(8192, 14336, 6144) == 4 and d(8192, 4096, 14336) == 4 and d(8192, 14336, 256) == 4
     assert d(512, 14336, 4096) == 3 and d(512, 4096, 4096) == 2
 
 
