@@ -1244,8 +1244,8 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
   switch (algo) {
     case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, 1>(a, stream);
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
-    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 3>(a, stream);
-    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 3>(a, stream);
+    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8>(a, stream);
+    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
