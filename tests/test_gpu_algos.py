@@ -21,7 +21,10 @@ SHAPES = [("all_algos", 7, 1040, 1024, E4, E4, True), ("tiled", 300, 4112, 640, 
           # one activation row, 7 wavefronts of 2 units each, 16 and 32 rows per workgroup
           ("decode_one_row", 1, 6144, 14336, E5, E4, True),
           # 20 units over 7 wavefronts (3, 3, ..., 2), several activation rows
-          ("decode_uneven_units", 5, 2080, 20480, E4, E4, False)]
+          ("decode_uneven_units", 5, 2080, 20480, E4, E4, False),
+          # 17 k steps: two whole 8-step metadata blocks, then one step in the
+          # reused first buffer; ragged tiles in m and n
+          ("tiled_partial_block", 264, 1040, 2176, E4, E5, True)]
 
 
 @pytest.fixture(scope="module", autouse=True)
