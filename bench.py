@@ -66,7 +66,8 @@ TRAFFIC_SOURCES = ("sparse_fp8_row_amd/csrc/gemm.hip", "sparse_fp8_row_amd/csrc/
 TRAFFIC_FILE = "profiles/traffic_linear_prefill_up.txt"
 # the kernel behind each configuration the prefill workload can take
 ALGO_KERNELS = {2: "linear_tiled_kernel (64x64 tile, 4 wavefronts)", 3: "linear_tiled_kernel (128x128 tile, 4 wavefronts)",
-                4: "linear_tiled_kernel (256x256 tile, 8 wavefronts)", 5: "linear_wide_kernel (256x256 tile, 4 wavefronts)"}
+                4: "linear_persistent_kernel (256x256 tile, 8 wavefronts, one workgroup per CU)",
+                5: "linear_wide_kernel (256x256 tile, 4 wavefronts)"}
 COPY_BYTES = 1 << 30
 
 

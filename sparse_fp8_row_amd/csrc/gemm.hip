@@ -38,6 +38,7 @@
 //    their partial 16x16 sums through LDS in a fixed order (deterministic).
 //    Tokens beyond M are zero columns of B, the padding-to-16 idea of
 //    pytorch/ao PR #1734 ("promote blocksparse from prototype ...").
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -464,6 +465,264 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
                                       smem + wave * (C::FN * C::FM * 512));
   } else {
     store_tile<OUT>(acc, xs, ws, bias, out, M, N, m0 + wm * C::TM, n0 + wn * C::TN, r16, lg, xs_stride, ws_stride);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent 256 x 256 kernel (bf16 output)
+// ---------------------------------------------------------------------------
+// The tiled kernel's scheme (two 48 KB stages, metadata in 8-step blocks,
+// eight wavefronts of 64(n) x 128(m), one barrier per k step) with three
+// changes:
+//  * global -> LDS loads through buffer descriptors based at the tile's first
+//    row: the k step and each load's row offset are scalar, so a load needs
+//    one vector offset per operand kind instead of a 64-bit address each, and
+//    rows past the matrix edge read zeros (those outputs are never stored);
+//  * wavefronts 0-3 issue every load and wait for them; wavefronts 4-7 never
+//    wait on the memory counter (gfx9 counts stores in it too), so they can
+//    issue a tile's output stores and go straight on into the next tile;
+//  * one workgroup per CU walks its XCD's run of tiles: the next tile's first
+//    stage and metadata block are put in flight before the output is staged,
+//    so their latency overlaps the epilogue.
+// Epilogue per half of the tile: every wavefront writes its scaled bf16 rows
+// into its own 8 KB LDS region (in stage slot 1 and metadata buffer 1, which
+// the next tile's first loads do not touch), then the store wavefronts each
+// write two regions out as whole 128-byte row segments.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  // raw buffer, 32-bit data format in the last descriptor word (gfx9)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One 1 KB buffer -> LDS load: lane l's 16 bytes at voff + soff land at lds + 16 l.
+__device__ __forceinline__ void buffer_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  // the LDS address and the scalar offset are uniform; saying so keeps the
+  // compiler from looping over their values
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(uintptr_t)a, 16, voff, __builtin_amdgcn_readfirstlane(soff), 0,
+                                           0);
+}
+
+// Loads of one 256 x 256 tile, shared by NL wavefronts (lw = 0 .. NL-1).  LDS
+// layouts are those of the tiled kernel: a stage is 16 1 KB blocks of weight
+// values then 32 of activation; a metadata block 32 1 KB blocks.
+template <int NL>
+struct TileBufferLoader {
+  static constexpr int BN = 256, BM = 256, MB = 8;
+  static constexpr int W_INSTR = BN / 16, X_INSTR = BM / 8, M_INSTR = BN / 8;
+  static constexpr int W_PW = W_INSTR / NL, X_PW = X_INSTR / NL, M_PW = M_INSTR / NL;
+  static_assert(W_INSTR % NL == 0 && X_INSTR % NL == 0 && M_INSTR % NL == 0, "loads split evenly");
+  __amdgpu_buffer_rsrc_t rx, rw, rm;
+  int ldx, ldv, ldm, vx, vw, lw, lane;
+  // requires 256 * K < 2^31 (every offset and range fits the descriptor)
+  __device__ TileBufferLoader(const uint8_t* xq, const uint8_t* values, const uint8_t* meta, int M, int N, int K, int m0,
+                              int n0, int lw_, int lane_)
+      : ldx(K), ldv(K / 2), ldm(K / 8), lw(lw_), lane(lane_) {
+    const int rows_m = min(M - m0, BM), rows_n = min(N - n0, BN);
+    rx = buffer_rsrc(xq + (int64_t)m0 * K, rows_m * K);
+    rw = buffer_rsrc(values + (int64_t)n0 * (K / 2), rows_n * (K / 2));
+    rm = buffer_rsrc(meta + (int64_t)n0 * (K / 8), rows_n * (K / 8));
+    // lane -> (row within the load, swizzled 16-byte chunk), as in StageLoader
+    vx = (lane >> 3) * ldx + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+    vw = (lane >> 2) * ldv + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+  }
+  __device__ __forceinline__ void stage(uint8_t* base, int kt) const {
+#pragma unroll
+    for (int j = 0; j < W_PW; ++j)
+      buffer_lds16(rw, base + (lw * W_PW + j) * 1024, vw, (lw * W_PW + j) * 16 * ldv + kt * 64);
+#pragma unroll
+    for (int q = 0; q < X_PW; ++q)
+      buffer_lds16(rx, base + (W_INSTR + lw * X_PW + q) * 1024, vx, (lw * X_PW + q) * 8 * ldx + kt * 128);
+  }
+  // metadata block blk: row r's chunk of step s at chunk s ^ (r % 8); chunks
+  // past the last k step repeat that step's chunk
+  __device__ __forceinline__ void metablock(uint8_t* buf, int blk, int KT) const {
+    const int s = min((lane & 7) ^ ((lane >> 3) & 7), KT - MB * blk - 1);
+    const int vm = (lane >> 3) * ldm + 16 * s;
+#pragma unroll
+    for (int j = 0; j < M_PW; ++j)
+      buffer_lds16(rm, buf + (lw * M_PW + j) * 1024, vm, (lw * M_PW + j) * 8 * ldm + 16 * MB * blk);
+  }
+};
+
+template <int XF, int WF, int G>
+__global__ __launch_bounds__(512, 1) void linear_persistent_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
+    const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
+  constexpr int BN = 256, BM = 256, WN = 4, WM = 2, S = 2, MB = 8, NL = 4;
+  using C = Tiled<BN, BM, WN, WM, S, MB>;
+  using L = TileBufferLoader<NL>;
+  static_assert(C::NW == 8 && C::FM == 8 && C::TN == 64, "epilogue regions: 8 KB per wavefront half");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  // ---- tiles: XCD x (workgroup id mod 8) owns a contiguous run, grouped
+  // along n as in the tiled kernel; its workgroups take every nslot-th ----
+  const int T = tiles_m * tiles_n;
+  const int per_xcd = (T + 7) / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, nslot = gridDim.x / 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave / WM, wm = wave % WM;
+  const int r16 = lane & 15, lg = lane >> 4;
+  const bool loader_wave = wave < NL;
+  const int lw = loader_wave ? wave : 0;
+  const int KT = K / KSTEP;
+  auto tile_of = [&](int it, int& n0, int& m0) -> bool {
+    const int j = slot + nslot * it;
+    if (j >= per_xcd) return false;
+    const int lid = xcd * per_xcd + j;
+    if (lid >= T) return false;
+    const int group = lid / (G * tiles_m);
+    const int first_n = group * G;
+    const int gsize = min(tiles_n - first_n, G);
+    const int within = lid - group * G * tiles_m;
+    n0 = (first_n + within % gsize) * BN;
+    m0 = (within / gsize) * BM;
+    return true;
+  };
+
+  // ---- LDS read offsets (as in the tiled kernel with MB = 8) ----
+  uint8_t* const meta_lds = smem + S * C::STAGE;
+  int a_off[C::FN], i_off[C::FN], b_off0[C::FM], b_off1[C::FM];
+#pragma unroll
+  for (int f = 0; f < C::FN; ++f) {
+    const int r = wn * C::TN + f * 16 + r16;
+    a_off[f] = r * 64 + 16 * w_chunk(r, lg);
+    i_off[f] = (int)(meta_lds - smem) + r * (16 * MB) + 4 * lg;
+  }
+#pragma unroll
+  for (int f = 0; f < C::FM; ++f) {
+    const int r = wm * C::TM + f * 16 + r16;
+    b_off0[f] = C::W_BYTES + r * 128 + 16 * x_chunk(r, lg);
+    b_off1[f] = C::W_BYTES + r * 128 + 16 * x_chunk(r, 4 + lg);
+  }
+  // epilogue regions: stage slot 1 holds six, metadata buffer 1 two
+  auto region = [&](int w) -> uint8_t* {
+    return w < 6 ? smem + C::STAGE + w * 8192 : meta_lds + C::META_BLOCK + (w - 6) * 8192;
+  };
+
+  int n0, m0;
+  if (!tile_of(0, n0, m0)) return;
+  if (loader_wave) {
+    const L first(xq, values, meta, M, N, K, m0, n0, lw, lane);
+    first.metablock(meta_lds, 0, KT);
+    first.stage(smem, 0);
+  }
+  for (int it = 0;; ++it) {
+    const L loader(xq, values, meta, M, N, K, m0, n0, lw, lane);
+    v4f acc[C::FN][C::FM];
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = 0; kt < KT; ++kt) {
+      // the loaders' loads of stage kt (and of its metadata block) have
+      // landed once they have none pending; the barrier tells everyone
+      if (loader_wave) wait_vmcnt<0>();
+      stage_barrier();
+      if (loader_wave) {
+        if (kt % MB == 0 && kt + MB < KT)
+          loader.metablock(meta_lds + ((kt / MB + 1) & 1) * C::META_BLOCK, kt / MB + 1, KT);
+        if (kt + 1 < KT) loader.stage(smem + ((kt + 1) % S) * C::STAGE, kt + 1);
+      }
+      const uint8_t* base = smem + (kt % S) * C::STAGE;
+      const int mo = 16 * ((kt % MB) ^ (r16 & 7)) + ((kt / MB) & 1) * C::META_BLOCK - (int)(base - smem);
+      v8i b[C::FM];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+        b[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      v4i a[2];
+      int idx[2];
+      a[0] = *reinterpret_cast<const v4i*>(base + a_off[0]);
+      idx[0] = *reinterpret_cast<const int*>(base + i_off[0] + mo);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        if (fn + 1 < C::FN) {
+          a[(fn + 1) & 1] = *reinterpret_cast<const v4i*>(base + a_off[fn + 1]);
+          idx[(fn + 1) & 1] = *reinterpret_cast<const int*>(base + i_off[fn + 1] + mo);
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+          acc[fn][fm] = smfmac16<XF, WF>(a[fn & 1], b[fm], acc[fn][fm], idx[fn & 1]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+
+    // ---- epilogue ----
+    int nn0 = 0, nm0 = 0;
+    const bool next = tile_of(it + 1, nn0, nm0);
+    const int mb = m0 + wm * C::TM, nb = n0 + wn * C::TN;
+    float xsv[C::FM];
+    v4f wsv[C::FN];
+    uint2 bv[C::FN];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) xsv[fm] = xs[min(mb + fm * 16 + r16, M - 1) * xs_stride];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int nc = min(nb + fn * 16 + 4 * lg, N - 4);
+      wsv[fn] = load_ws4(ws, nc, ws_stride);
+      bv[fn] = bias ? *reinterpret_cast<const uint2*>(bias + nc) : make_uint2(0u, 0u);
+    }
+    lds_barrier();  // every wavefront is done with the last step's LDS reads
+    if (next && loader_wave) {
+      const L nl(xq, values, meta, M, N, K, nm0, nn0, lw, lane);
+      nl.metablock(meta_lds, 0, KT);
+      nl.stage(smem, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // rows m = wm * 128 + 64 h .. + 63 of this wavefront's block, 128 bytes
+      // each, 16-byte chunk c at c ^ (row % 8)
+      uint8_t* reg = region(wave);
+#pragma unroll
+      for (int q = 0; q < C::FM / 2; ++q) {
+        const int fm = h * (C::FM / 2) + q, row = q * 16 + r16;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          v4f y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = acc[fn][fm][i] * (xsv[fm] * wsv[fn][i]);
+          if (bias) {
+            y[0] += bf16_to_f32(bv[fn].x & 0xFFFFu);
+            y[1] += bf16_to_f32(bv[fn].x >> 16);
+            y[2] += bf16_to_f32(bv[fn].y & 0xFFFFu);
+            y[3] += bf16_to_f32(bv[fn].y >> 16);
+          }
+          const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+          const int c = (2 * fn + (lg >> 1)) ^ (row & 7);
+          *reinterpret_cast<uint2*>(reg + row * 128 + c * 16 + 8 * (lg & 1)) = make_uint2(lo, hi);
+        }
+      }
+      lds_barrier();  // every region written
+      if (!loader_wave) {
+        // N is a multiple of 16, so a chunk starting below N lies inside the row
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int sw = 2 * (wave - NL) + q;
+          const int swn = sw / WM, swm = sw % WM;
+          const uint8_t* sreg = region(sw);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int row = t * 8 + (lane >> 3), c = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4*>(sreg + row * 128 + 16 * (c ^ (row & 7)));
+            const int m = m0 + swm * C::TM + h * 64 + row, n = n0 + swn * C::TN + 8 * c;
+            if (m < M && n < N) *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = v;
+          }
+        }
+      }
+      lds_barrier();  // the store wavefronts have read every region
+    }
+    if (!next) break;
+    n0 = nn0;
+    m0 = nm0;
   }
 }
 
@@ -968,6 +1227,43 @@ hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The persistent kernel needs every per-tile offset in 32 bits.
+inline bool persistent_ok(const LinearArgs& a) { return a.k * 256 < ((int64_t)1 << 31); }
+
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 8) c = 256;
+    cus[dev] = c;  // benign race: every thread stores the same value
+  }
+  return cus[dev];
+}
+
+template <int XF, int WF, int G>
+hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
+  using C = Tiled<256, 256, 4, 2, 2, 8>;
+  const int tiles_m = (int)((a.m + 255) / 256), tiles_n = (int)((a.n + 255) / 256);
+  const int T = tiles_m * tiles_n;
+  // a multiple of 8 workgroups (the XCD mapping), at most one per CU
+  const int grid = std::max(8, std::min(8 * ((T + 7) / 8), (device_cus() / 8) * 8));
+  auto kern = linear_persistent_kernel<XF, WF, G>;
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws, a.bias,
+                     reinterpret_cast<uint16_t*>(a.out), (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride,
+                     a.ws_stride);
+  return hipGetLastError();
+}
+
 // Wavefronts per workgroup of the unit decode kernel: the K / 1024 units
 // spread evenly over at most 8 wavefronts.
 inline int unit_waves(int64_t k) {
@@ -1246,7 +1542,9 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
     case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8>(a, stream);
-    case ALGO_TILED_256: return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
+    case ALGO_TILED_256:
+      if (OUT == OUT_BF16 && persistent_ok(a)) return run_persistent<XF, WF, 8>(a, stream);
+      return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
   }
