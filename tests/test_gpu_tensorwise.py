@@ -68,9 +68,9 @@ def test_tensorwise_quantize_deterministic(gpu):
     assert host_f32(outs[0][1])[0] == host_f32(outs[1][1])[0]
 
 
-# (name, m, n, k, kernel): decode, tiled, pipelined 256x256
+# (name, m, n, k): decode, tiled, persistent 256x256 (ragged in m and n)
 LINEAR_SHAPES = [("decode1", 1, 4096, 4096), ("decode16", 16, 4096, 4096), ("tiled", 100, 1040, 384),
-                 ("wide", 4100, 8208, 512)]
+                 ("persistent", 4100, 8208, 512)]
 KINDS = [("tensor", "row"), ("row", "tensor"), ("tensor", "tensor")]
 
 
