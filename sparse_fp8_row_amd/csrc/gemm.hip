@@ -1589,10 +1589,17 @@ int linear_default_algo(int64_t m, int64_t n, int64_t k) {
     if (m >= 2 && n >= 6144 && linear_algo_supported(ALGO_DECODE_LDS_32, m, n, k)) return ALGO_DECODE_LDS_32;
     return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
   }
-  const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
-  const int64_t mid = ((m + 127) / 128) * ((n + 127) / 128);
-  if (big >= 512) return ALGO_TILED_256;
-  if (mid >= 256) return ALGO_TILED_128;
+  // Rounds of tiles over the CUs: one 256x256 tile per CU at a time, two
+  // 128x128 ones.  A 128x128 round takes about 0.65 of a 256x256 one
+  // (measured on the Llama shapes at M = 1024..4096), so the 256x256
+  // configuration wins once it needs at most 2/3 as many rounds, and always
+  // from two full rounds on.
+  const int64_t cus = device_cus();
+  const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+  const int64_t r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
+  if (t256 >= 2 * cus || 3 * r256 <= 2 * r128) return ALGO_TILED_256;
+  if (t128 >= cus) return ALGO_TILED_128;
   return ALGO_TILED_64;
 }
 

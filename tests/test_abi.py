@@ -182,6 +182,9 @@ def test_linear_algos(lib):
     assert d(16, 6144, 640) == 1 and d(4, 6160, 4096) == 0
     assert d(8192, 14336, 4096) == 4 and d(8192, 14336, 6144) == 4 and d(8192, 4096, 14336) == 4 and d(8192, 14336, 256) == 4
     assert d(512, 14336, 4096) == 3 and d(512, 4096, 4096) == 2
+    # 256x256 tiles from 2/3 of the 128x128 configuration's rounds (256 CUs without a GPU)
+    assert d(1024, 14336, 4096) == 4 and d(2048, 4096, 4096) == 3 and d(4096, 4096, 14336) == 4
+    assert d(2048, 4096, 14336) == 3 and d(1024, 6144, 4096) == 3
 
 
 def test_linear_algo_validation(lib):
