@@ -504,18 +504,18 @@ __device__ __forceinline__ void buffer_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* 
                                            0);
 }
 
-// Loads of one 256 x 256 tile, shared by NL wavefronts (lw = 0 .. NL-1).  LDS
-// layouts are those of the tiled kernel: a stage is 16 1 KB blocks of weight
-// values then 32 of activation; a metadata block 32 1 KB blocks.
-template <int NL>
+// Loads of one BN x BM tile, shared by NL wavefronts (lw = 0 .. NL-1).  LDS
+// layouts are those of the tiled kernel: a stage is BN / 16 1 KB blocks of
+// weight values then BM / 8 of activation; a metadata block BN / 8 blocks.
+template <int BN, int BM, int NL>
 struct TileBufferLoader {
-  static constexpr int BN = 256, BM = 256, MB = 8;
+  static constexpr int MB = 8;
   static constexpr int W_INSTR = BN / 16, X_INSTR = BM / 8, M_INSTR = BN / 8;
   static constexpr int W_PW = W_INSTR / NL, X_PW = X_INSTR / NL, M_PW = M_INSTR / NL;
   static_assert(W_INSTR % NL == 0 && X_INSTR % NL == 0 && M_INSTR % NL == 0, "loads split evenly");
   __amdgpu_buffer_rsrc_t rx, rw, rm;
   int ldx, ldv, ldm, vx, vw, lw, lane;
-  // requires 256 * K < 2^31 (every offset and range fits the descriptor)
+  // requires max(BN, BM) * K < 2^31 (every offset and range fits the descriptor)
   __device__ TileBufferLoader(const uint8_t* xq, const uint8_t* values, const uint8_t* meta, int M, int N, int K, int m0,
                               int n0, int lw_, int lane_)
       : ldx(K), ldv(K / 2), ldm(K / 8), lw(lw_), lane(lane_) {
@@ -546,15 +546,20 @@ struct TileBufferLoader {
   }
 };
 
-template <int XF, int WF, int G>
-__global__ __launch_bounds__(512, 1) void linear_persistent_kernel(
+template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC>
+__global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
-  constexpr int BN = 256, BM = 256, WN = 4, WM = 2, S = 2, MB = 8, NL = 4;
+  constexpr int S = 2, MB = 8;
   using C = Tiled<BN, BM, WN, WM, S, MB>;
-  using L = TileBufferLoader<NL>;
-  static_assert(C::NW == 8 && C::FM == 8 && C::TN == 64, "epilogue regions: 8 KB per wavefront half");
+  using L = TileBufferLoader<BN, BM, NL>;
+  // epilogue: each wavefront stages half its block (TM / 2 rows of 128 bytes)
+  // per pass; the NW - NL store wavefronts write out PER regions each
+  constexpr int RB = C::TM / 2 * 128, PER = C::NW / (C::NW - NL);
+  static_assert(C::TN == 64 && C::FM % 2 == 0, "128-byte rows of whole 16x16 blocks");
+  static_assert(NL > 0 && NL < C::NW && C::NW % (C::NW - NL) == 0, "loader and store wavefronts");
+  static_assert(C::NW * RB <= C::STAGE + C::META_BLOCK, "regions fit in stage slot 1 and metadata buffer 1");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // ---- tiles: XCD x (workgroup id mod 8) owns a contiguous run, grouped
@@ -598,9 +603,10 @@ __global__ __launch_bounds__(512, 1) void linear_persistent_kernel(
     b_off0[f] = C::W_BYTES + r * 128 + 16 * x_chunk(r, lg);
     b_off1[f] = C::W_BYTES + r * 128 + 16 * x_chunk(r, 4 + lg);
   }
-  // epilogue regions: stage slot 1 holds six, metadata buffer 1 two
+  // epilogue regions: stage slot 1 first, then metadata buffer 1
+  constexpr int IN_SLOT = C::STAGE / RB;
   auto region = [&](int w) -> uint8_t* {
-    return w < 6 ? smem + C::STAGE + w * 8192 : meta_lds + C::META_BLOCK + (w - 6) * 8192;
+    return w < IN_SLOT ? smem + C::STAGE + w * RB : meta_lds + C::META_BLOCK + (w - IN_SLOT) * RB;
   };
 
   int n0, m0;
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(512, 1) void linear_persistent_kernel(
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // rows m = wm * 128 + 64 h .. + 63 of this wavefront's block, 128 bytes
+      // rows m = wm * TM + h TM / 2 .. of this wavefront's block, 128 bytes
       // each, 16-byte chunk c at c ^ (row % 8)
       uint8_t* reg = region(wave);
 #pragma unroll
@@ -705,15 +711,15 @@ __global__ __launch_bounds__(512, 1) void linear_persistent_kernel(
       if (!loader_wave) {
         // N is a multiple of 16, so a chunk starting below N lies inside the row
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int sw = 2 * (wave - NL) + q;
+        for (int q = 0; q < PER; ++q) {
+          const int sw = PER * (wave - NL) + q;
           const int swn = sw / WM, swm = sw % WM;
           const uint8_t* sreg = region(sw);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
+          for (int t = 0; t < C::TM / 16; ++t) {
             const int row = t * 8 + (lane >> 3), c = lane & 7;
             const uint4 v = *reinterpret_cast<const uint4*>(sreg + row * 128 + 16 * (c ^ (row & 7)));
-            const int m = m0 + swm * C::TM + h * 64 + row, n = n0 + swn * C::TN + 8 * c;
+            const int m = m0 + swm * C::TM + h * (C::TM / 2) + row, n = n0 + swn * C::TN + 8 * c;
             if (m < M && n < N) *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = v;
           }
         }
@@ -1228,7 +1234,7 @@ hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
 }
 
 // The persistent kernel needs every per-tile offset in 32 bits.
-inline bool persistent_ok(const LinearArgs& a) { return a.k * 256 < ((int64_t)1 << 31); }
+inline bool persistent_ok(const LinearArgs& a, int tile) { return a.k * tile < ((int64_t)1 << 31); }
 
 // Compute units of the current device (cached per device).
 inline int device_cus() {
@@ -1243,14 +1249,14 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <int XF, int WF, int G>
+template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC>
 hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
-  using C = Tiled<256, 256, 4, 2, 2, 8>;
-  const int tiles_m = (int)((a.m + 255) / 256), tiles_n = (int)((a.n + 255) / 256);
+  using C = Tiled<BN, BM, WN, WM, 2, 8>;
+  const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
-  // a multiple of 8 workgroups (the XCD mapping), at most one per CU
-  const int grid = std::max(8, std::min(8 * ((T + 7) / 8), (device_cus() / 8) * 8));
-  auto kern = linear_persistent_kernel<XF, WF, G>;
+  // a multiple of 8 workgroups (the XCD mapping), at most OCC per CU
+  const int grid = std::max(8, std::min(8 * ((T + 7) / 8), (OCC * device_cus() / 8) * 8));
+  auto kern = linear_persistent_kernel<XF, WF, BN, BM, WN, WM, NL, G, OCC>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1543,7 +1549,7 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
     case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_256:
-      if (OUT == OUT_BF16 && persistent_ok(a)) return run_persistent<XF, WF, 8>(a, stream);
+      if (OUT == OUT_BF16 && persistent_ok(a, 256)) return run_persistent<XF, WF, 256, 256, 4, 2, 4, 8, 1>(a, stream);
       return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
