@@ -546,7 +546,8 @@ struct TileBufferLoader {
   }
 };
 
-template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC>
+// NT = 1: output stores are non-temporal.
+template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -720,7 +721,15 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
             const int row = t * 8 + (lane >> 3), c = lane & 7;
             const uint4 v = *reinterpret_cast<const uint4*>(sreg + row * 128 + 16 * (c ^ (row & 7)));
             const int m = m0 + swm * C::TM + h * (C::TM / 2) + row, n = n0 + swn * C::TN + 8 * c;
-            if (m < M && n < N) *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = v;
+            if (m < M && n < N) {
+              uint4* o = reinterpret_cast<uint4*>(out + (int64_t)m * N + n);
+              if constexpr (NT) {
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(o));
+              } else {
+                *o = v;
+              }
+            }
           }
         }
       }
@@ -1249,14 +1258,14 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC>
+template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
 hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, 2, 8>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   // a multiple of 8 workgroups (the XCD mapping), at most OCC per CU
   const int grid = std::max(8, std::min(8 * ((T + 7) / 8), (OCC * device_cus() / 8) * 8));
-  auto kern = linear_persistent_kernel<XF, WF, BN, BM, WN, WM, NL, G, OCC>;
+  auto kern = linear_persistent_kernel<XF, WF, BN, BM, WN, WM, NL, G, OCC, NT>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1549,7 +1558,9 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
     case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8>(a, stream);
     case ALGO_TILED_256:
-      if (OUT == OUT_BF16 && persistent_ok(a, 256)) return run_persistent<XF, WF, 256, 256, 4, 2, 4, 8, 1>(a, stream);
+      // non-temporal output stores: the GEMM's speed is the same, and the
+      // next kernel's traffic no longer waits behind its dirty lines
+      if (OUT == OUT_BF16 && persistent_ok(a, 256)) return run_persistent<XF, WF, 256, 256, 4, 2, 4, 8, 1, 1>(a, stream);
       return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
