@@ -115,10 +115,11 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float
   }
 }
 
-// bf16 epilogue through LDS.  The accumulator layout gives each store
-// instruction 16 rows x 32 bytes, and output written that way reached about
-// half of what plain full-line writes reach (3.6 against 7 TB/s), which made
-// the stores of the 256 x 256 kernel a fifth of its time.  So a wavefront
+// bf16 epilogue through LDS (NT = 1: non-temporal stores).  The accumulator
+// layout gives each store instruction 16 rows x 32 bytes, and output written
+// that way reached about half of what plain full-line writes reach (3.6
+// against 7 TB/s), which made the stores of the 256 x 256 kernel a fifth of
+// its time.  So a wavefront
 // writes its finished FN x FM block, scaled and rounded, row-major into
 // `region` (FM * 16 rows of FN * 32 bytes, each 16-byte chunk at
 // chunk ^ (row % chunks-per-row) so the writes and the reads spread over the
@@ -128,7 +129,7 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[FN][FM], const float
 // multiple of 16 (checked at the boundary), so a chunk that starts below N
 // lies wholly inside the row.  The caller makes the LDS free first (every
 // wavefront done with its last stage); each wavefront uses only its own region.
-template <int FN, int FM>
+template <int FN, int FM, int NT = 0>
 __device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[FN][FM], const float* __restrict__ xs,
                                                     const float* __restrict__ ws, const uint16_t* __restrict__ bias,
                                                     uint16_t* __restrict__ out, int M, int N, int mb, int nb, int r16,
@@ -174,7 +175,15 @@ __device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[FN][FM], co
     const int row = t * RPI + lane / CPR, c = lane % CPR;
     const uint4 v = *reinterpret_cast<const uint4*>(region + row * (CPR * 16) + 16 * (c ^ (row & (CPR - 1))));
     const int m = mb + row, n = nb + 8 * c;
-    if (m < M && n < N) *reinterpret_cast<uint4*>(out + (int64_t)m * N + n) = v;
+    if (m < M && n < N) {
+      uint4* o = reinterpret_cast<uint4*>(out + (int64_t)m * N + n);
+      if constexpr (NT) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(o));
+      } else {
+        *o = v;
+      }
+    }
   }
 }
 
@@ -314,7 +323,7 @@ struct StageLoader {
   }
 };
 
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC, int MB>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC, int MB, int NT>
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -460,7 +469,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   // wavefront is done with the last stage) ----
   if constexpr (OUT == OUT_BF16) {
     lds_barrier();
-    store_tile_bf16_lds<C::FN, C::FM>(acc, xs, ws, bias, reinterpret_cast<uint16_t*>(out), M, N, m0 + wm * C::TM,
+    store_tile_bf16_lds<C::FN, C::FM, NT>(acc, xs, ws, bias, reinterpret_cast<uint16_t*>(out), M, N, m0 + wm * C::TM,
                                       n0 + wn * C::TN, r16, lg, lane, xs_stride, ws_stride,
                                       smem + wave * (C::FN * C::FM * 512));
   } else {
@@ -1223,13 +1232,14 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1, int MB = 0>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1, int MB = 0,
+          int NT = 0>
 hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, S, MB>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC, MB>;
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC, MB, NT>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1555,13 +1565,13 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
   switch (algo) {
     case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, 1>(a, stream);
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
-    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8>(a, stream);
-    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8>(a, stream);
+    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
+    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
     case ALGO_TILED_256:
       // non-temporal output stores: the GEMM's speed is the same, and the
       // next kernel's traffic no longer waits behind its dirty lines
       if (OUT == OUT_BF16 && persistent_ok(a, 256)) return run_persistent<XF, WF, 256, 256, 4, 2, 4, 8, 1, 1>(a, stream);
-      return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8>(a, stream);
+      return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8, 1>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
     default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
   }
