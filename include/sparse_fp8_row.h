@@ -242,7 +242,11 @@ sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, 
  *   sfr_linear_algo_supported(a, m, n, k)
  *                                1 if algorithm a can run the shape, else 0.
  *   sfr_linear_default_algo(m, n, k)
- *                                the library's built-in choice for the shape.
+ *                                the library's built-in choice for the shape
+ *                                on the current device (it counts rounds of
+ *                                tiles over the device's compute units, so it
+ *                                can differ between GPUs; 256 units are
+ *                                assumed when no device is present).
  *   sparse_fp8_scaled_linear_algo(..., algo, stream)
  *                                sparse_fp8_scaled_linear with the given
  *                                algorithm; SFR_ALGO_DEFAULT (-1) = built-in
