@@ -146,6 +146,14 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
                                                          const uint16_t* __restrict__ values, int64_t N,
                                                          const uint16_t* __restrict__ bias, void* __restrict__ out) {
   __shared__ v4f red[NW][64];
+  // each wavefront's U 2 KB block slices (16 rows x 128 bytes), filled by
+  // global->LDS loads of whole lines: load h of a slice takes rows 8h..8h+7,
+  // lane l the 16-byte chunk (l % 8) ^ (row % 8) of row 8h + l / 8, written
+  // at 16 l -- so chunk c of row r sits at chunk c ^ (r % 8), and the
+  // operand reads of 8 consecutive rows at one chunk hit distinct banks.
+  // (Loaded as MFMA operands straight from memory, each 1 KB load touched
+  // 16 half lines.)
+  __shared__ __attribute__((aligned(1024))) uint8_t wbuf[NW][U * 2048];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t tiles_n = N / 16;
@@ -154,32 +162,53 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
   const int j0 = crow[br], j1 = crow[br + 1];
   const int64_t kmax = K / BS - 1;
   const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (int64_t)min(m0 + r16, M - 1) * K) + 16 * g;
-  const uint8_t* vrow = reinterpret_cast<const uint8_t*>(values) + (rowoff + r16) * (BS * 2) + 16 * g;
+  // this lane's part of a slice load, and its operand chunks (step s: k = 32 s + 8 g .. + 7)
+  const uint8_t* vload = reinterpret_cast<const uint8_t*>(values) + (rowoff + (lane >> 3)) * (BS * 2) +
+                         16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  const int a_rd0 = r16 * 128 + 16 * (g ^ (r16 & 7)), a_rd1 = r16 * 128 + 16 * ((4 + g) ^ (r16 & 7));
+  uint8_t* const mine = wbuf[wave];
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  // the block columns of a group (lane u holds block u's) are loaded one
+  // group ahead, so the activation addresses are ready before the group's
+  // global->LDS loads go out (a wait for an ordinary load would also wait
+  // for those)
+  int cv = j0 + wave < j1 ? col[min(j0 + wave + NW * min(lane, U - 1), j1 - 1)] : 0;
   for (int jb = j0 + wave; jb < j1; jb += NW * U) {
     const int live = min(U, (j1 - jb + NW - 1) / NW);  // blocks of this group (uniform)
     v4i a[U][2], b[U][2];
-    // the weight blocks need only the block index: their loads go out with
-    // the load of the group's block columns (lane u holds block u's), and
-    // only the activation loads wait for the columns
-    const int cv = col[min(jb + NW * min(lane, U - 1), j1 - 1)];
+    const uint8_t* xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // a corrupt index is clamped so the activation read stays inside x
+      const int64_t bc = min((int64_t)(uint32_t)__builtin_amdgcn_readlane(cv, u), kmax);
+      xb[u] = xrow + bc * (BS * 2);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < live) {
-        const uint8_t* vb = vrow + (int64_t)(jb + NW * u) * (BS * BS * 2);
+        const uint8_t* vb = vload + (int64_t)(jb + NW * u) * (BS * BS * 2);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) a[u][s] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vb + 64 * s));
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_global_load_lds((void*)(vb + h * 8 * (BS * 2)), (void*)(mine + u * 2048 + h * 1024), 16, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < live) {
-        // a corrupt index is clamped so the activation read stays inside x
-        const int64_t bc = min((int64_t)(uint32_t)__builtin_amdgcn_readlane(cv, u), kmax);
-        const uint8_t* xb = xrow + bc * (BS * 2);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) b[u][s] = *reinterpret_cast<const v4i*>(xb + 64 * s);
+        for (int s = 0; s < 2; ++s) b[u][s] = *reinterpret_cast<const v4i*>(xb[u] + 64 * s);
+      }
+    }
+    // the next group's block columns (clamped into this block row)
+    cv = col[min(jb + NW * U + NW * min(lane, U - 1), j1 - 1)];
+    // every load has landed (the activation loads and the global->LDS ones
+    // share the counter); then the slices' operand chunks
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters at maximum (gfx9 encoding)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < live) {
+        a[u][0] = *reinterpret_cast<const v4i*>(mine + u * 2048 + a_rd0);
+        a[u][1] = *reinterpret_cast<const v4i*>(mine + u * 2048 + a_rd1);
       }
     }
 #pragma unroll
@@ -194,6 +223,7 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
         }
       }
     }
+    // the LDS reads above fed the MFMAs, so the slices are free for the next group
   }
   red[wave][lane] = acc0 + acc1;
   __syncthreads();
