@@ -129,7 +129,7 @@ sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols
                                    void* stream);
 
 /* Workspace bytes quantize_tensorwise_fp8 needs for a [rows, cols] tensor
- * (at most 2 KB); 0 for sizes it rejects. */
+ * (at most 4 KB); 0 for sizes it rejects. */
 int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols);
 
 /*

@@ -106,7 +106,7 @@ def test_linear_validation(lib):
 
 def test_tensorwise_quantize_validation(lib):
     wb = lib.sfr_quantize_tensorwise_workspace_bytes
-    assert wb(8192, 4096) == 2048                       # 512 blocks of 8192 chunks
+    assert wb(8192, 4096) == 4096                       # 1024 blocks of 4096 chunks
     assert wb(16, 4096) == 4 * (16 * 4096 // 8 // 256)  # blocks of 256 chunks
     assert wb(1, 8) == 4
     assert wb(4, 15) == 0 and wb(0, 16) == 0 and wb(-1, 16) == 0
