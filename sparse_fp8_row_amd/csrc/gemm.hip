@@ -1372,20 +1372,6 @@ __device__ __forceinline__ void fused_first_loads(uint8_t* __restrict__ xl, uint
     for (int h = 0; h < 2; ++h) xa[c][h] = reinterpret_cast<const uint4*>(xl + (2 * c + h) * 1024)[lane];
 }
 
-// Wavefront maximum without LDS-path instructions (DPP row shifts, readlane).
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t m) {
-  // row_shr 1, 2, 4, 8 (DPP controls 0x111 .. 0x118; lanes shifted in from
-  // outside the 16-lane row read 0): lane 15 of each row ends with the row's
-  // maximum
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
-  return max(max(a, b), max(c, d));
-}
-
 template <int XF, int WF, int OUT, int NWMAX>
 __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_unit_fused1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
@@ -1454,7 +1440,7 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
 #pragma unroll
   for (int c = 0; c < UPW; ++c)
     if (c < nuw) mx = mag_max8(xa[c][1], mag_max8(xa[c][0], mx));
-  mx = wave_max_dpp(mx);
+  mx = wave_max(mx);
   if (lane == 0) wmax[wave] = mx;
   lds_barrier();
   uint32_t mm = wmax[0];

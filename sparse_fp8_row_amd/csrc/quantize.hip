@@ -65,6 +65,9 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
         const int64_t c = lane + 64 * i;
         if (c < nchunks) qr[c] = zero8(buf[i]);
       }
+    } else if (nchunks == 64 * R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) qr[lane + 64 * i] = cast8<FMT>(buf[i], s, r);
     } else {
 #pragma unroll
       for (int i = 0; i < R; ++i) {

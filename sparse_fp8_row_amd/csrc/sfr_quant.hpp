@@ -18,10 +18,18 @@ __device__ __forceinline__ uint32_t mag_max8(uint4 c, uint32_t m) {
   return m;
 }
 
+// Wavefront maximum, uniform in every lane, without LDS-path instructions:
+// DPP row_shr 1, 2, 4, 8 (controls 0x111 .. 0x118; lanes shifted in from
+// outside the 16-lane row read 0) leave each row's maximum in its lane 15,
+// then four readlanes.
 __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  return m;
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+  return max(max(a, b), max(c, d));
 }
 
 // True when q = fl32(x * rcp) is known to encode to the same FP8 code as
@@ -32,9 +40,11 @@ __device__ __forceinline__ bool quotient_settled(float x, float q) {
   constexpr uint32_t kLowMask = (FMT == FMT_E4M3) ? 0xFFFFFu : 0x1FFFFFu;
   constexpr uint32_t kMid = (FMT == FMT_E4M3) ? 0x80000u : 0x100000u;
   const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
-  const uint32_t low = b & kLowMask;
-  const uint32_t dist = low > kMid ? low - kMid : kMid - low;
-  return (b >= kMinNormal && b < 0x7F800000u && dist > 8u) || x == 0.0f;
+  // |low - kMid| > 8, as one wrapping add and compare (low < kMid - 8 wraps
+  // to a large value)
+  const bool far = ((b & kLowMask) + (8u - kMid)) > 16u;
+  // bitwise, not short-circuit, so the test is straight-line code
+  return ((b >= kMinNormal) & (b < 0x7F800000u) & far) | (x == 0.0f);
 }
 
 // 8 bf16 -> 8 FP8 bytes.  `scale` > 0, `rcp` = fl32(1 / scale): the codes of
@@ -67,7 +77,7 @@ __device__ __forceinline__ uint2 cast8(uint4 c, float scale, float rcp) {
   for (int i = 0; i < 8; ++i) {
     // a zero keeps its sign (x * rcp would give NaN when rcp is infinite)
     t[i] = x[i] == 0.0f ? x[i] : x[i] * rcp;
-    settled = settled && quotient_settled<FMT>(x[i], t[i]);
+    settled &= quotient_settled<FMT>(x[i], t[i]);
   }
   if (__builtin_expect(!settled, 0)) {
 #pragma unroll
