@@ -40,7 +40,11 @@ def say(*a):
 # ---------------------------------------------------------------------------
 # quantize_rowwise_fp8
 # ---------------------------------------------------------------------------
-QSHAPES = [(1, 8), (3, 256), (17, 4096), (64, 4104), (5, 16384), (4, 16392), (130, 512), (9, 14336)]
+# rows <= 64 take the one-row-per-workgroup kernel; (80, 4096) and (66, 14336)
+# take the one-row-per-wavefront kernel with whole rows of 8 and 28 chunks per
+# lane (its unconditional load and store path), (70, 1000) its ragged path
+QSHAPES = [(1, 8), (3, 256), (17, 4096), (64, 4104), (5, 16384), (4, 16392), (130, 512), (9, 14336),
+           (80, 4096), (66, 14336), (70, 1000)]
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
