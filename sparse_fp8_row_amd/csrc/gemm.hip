@@ -242,7 +242,7 @@ struct Tiled {
   static_assert(BN % (16 * WN) == 0 && BM % (16 * WM) == 0, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(S >= 2, "stages");
-  static_assert(MB == 0 || (MB == 8 && S == 2 && BN % (8 * NW) == 0), "metadata blocks: 8 steps, two stages");
+  static_assert(MB == 0 || (MB == 8 && S >= 2 && S <= 9 && BN % (8 * NW) == 0), "metadata blocks: 8 steps");
 };
 
 // Global -> LDS loader of one pipeline stage.  The stage is W_INSTR + M_INSTR
@@ -405,7 +405,8 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
 
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once at most the loads of the S-2 later stages are
-    // pending (metadata blocks only with two stages: everything has landed)
+    // pending (a metadata block issued after stage kt only makes the wait
+    // stricter; it was issued at least one step earlier)
     if (kt + S - 2 < KT) wait_vmcnt<LPW * (S - 2)>();
     else wait_vmcnt<0>();
     stage_barrier();
@@ -1268,6 +1269,13 @@ inline int device_cus() {
   return cus[dev];
 }
 
+// Deep-pipeline form of a tiled configuration: at most `per_cu` tiles of
+// tile x tile per compute unit and K >= min_k.
+inline bool tiled_deep(const LinearArgs& a, int tile, int per_cu, int64_t min_k) {
+  const int64_t tiles = ((a.m + tile - 1) / tile) * ((a.n + tile - 1) / tile);
+  return a.k >= min_k && tiles <= (int64_t)per_cu * device_cus();
+}
+
 template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
 hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, 2, 8>;
@@ -1551,8 +1559,16 @@ hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
   switch (algo) {
     case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, 1>(a, stream);
     case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
-    case ALGO_TILED_64: return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
-    case ALGO_TILED_128: return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
+    // Four stages instead of two where few tiles share a CU (one or two
+    // workgroups per CU hide little latency by themselves) and K is long
+    // enough for the deeper pipeline to pay: each load then has three k steps
+    // to land.  Same arithmetic, same order, bit-identical output.
+    case ALGO_TILED_64:
+      if (tiled_deep(a, 64, 2, 8192)) return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
+    case ALGO_TILED_128:
+      if (tiled_deep(a, 128, 1, 4096)) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
     case ALGO_TILED_256:
       // non-temporal output stores: the GEMM's speed is the same, and the
       // next kernel's traffic no longer waits behind its dirty lines
