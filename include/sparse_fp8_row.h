@@ -253,9 +253,9 @@ sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, 
  *                                choice.  An id out of range is
  *                                SFR_ERR_DTYPE; an algorithm that cannot run
  *                                the shape is SFR_ERR_SHAPE.
- * Ids: 0 decode_lds (m <= 16, k % 1024 == 0), 1 decode_reg (m <= 16),
+ * Ids: 0 decode_lds (m <= 64, k % 1024 == 0), 1 decode_reg (m <= 16),
  * 2 tiled_64x64, 3 tiled_128x128, 4 tiled_256x256, 5 wide_256x256
- * (k >= 512), 6 decode_lds_32 (m <= 16, k % 1024 == 0, n % 32 == 0).
+ * (k >= 512), 6 decode_lds_32 (m <= 64, k % 1024 == 0, n % 32 == 0).
  */
 #define SFR_ALGO_DEFAULT (-1)
 int sfr_linear_algo_count(void);

@@ -1127,9 +1127,12 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(vrow_l * (K / 2) + 16 * (vc ^ ((2 * i + vrow_l) & 7)));
   const uint32_t moff = (uint32_t)(mrow_l * (K / 8) + 16 * (mc ^ (mrow_l & 7)));
-  // rows m >= M read row M - 1: MFMA output column m depends on activation
-  // row m alone, and those columns are never stored
-  const uint8_t* xrow = xq + (int64_t)min(r16, M - 1) * K + 16 * lg;
+  // workgroup row blockIdx.y takes activation rows mb .. mb + 15 (M up to
+  // 64: the weight block is read once per 16 rows, mostly from L2).  Rows
+  // past the last, Mc, read row Mc - 1: MFMA output column m depends on
+  // activation row m alone, and those columns are never stored
+  const int mb = blockIdx.y * 16, Mc = min(M - mb, 16);
+  const uint8_t* xrow = xq + (int64_t)(mb + min(r16, Mc - 1)) * K + 16 * lg;
   // LDS read offsets: step s's values chunk 4s + lg of row r16 sits at chunk
   // (4s + lg) ^ (r16 & 7) = 8 (s >> 1) + ab[s & 1]; its metadata chunk at s ^ (r16 & 7)
   const int r7 = r16 & 7;
@@ -1142,7 +1145,7 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
   v4f w4[RT];
   uint2 b2[RT];
   if (wave == 0) {
-    xsm = xs[min(m, M - 1) * xs_stride];
+    xsm = xs[(mb + min(m, Mc - 1)) * xs_stride];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int n = (blockIdx.x * RT + t) * 16 + 4 * lg;
@@ -1222,7 +1225,7 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
         y[2] += bf16_to_f32(b2[t].y & 0xFFFFu);
         y[3] += bf16_to_f32(b2[t].y >> 16);
       }
-      if (m < M) store4<OUT>(out, N, m, (blockIdx.x * RT + t) * 16 + 4 * lg, y);
+      if (m < Mc) store4<OUT>(out, N, mb + m, (blockIdx.x * RT + t) * 16 + 4 * lg, y);
     }
   }
 }
@@ -1316,7 +1319,8 @@ hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / (16 * RT))), dim3(64 * nw), lds, stream, a.xq, a.xs, a.values,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / (16 * RT)), (unsigned)((a.m + 15) / 16)), dim3(64 * nw), lds, stream,
+                     a.xq, a.xs, a.values,
                      a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
   return hipGetLastError();
 }
@@ -1595,13 +1599,13 @@ const char* linear_algo_name(int algo) {
 
 bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
   switch (algo) {
-    case ALGO_DECODE_LDS: return m <= 16 && k % kUnitK == 0;
+    case ALGO_DECODE_LDS: return m <= 64 && k % kUnitK == 0;
     case ALGO_DECODE_REG: return m <= 16;
     case ALGO_TILED_64:
     case ALGO_TILED_128:
     case ALGO_TILED_256: return true;
     case ALGO_WIDE_256: return k >= 4 * KSTEP;
-    case ALGO_DECODE_LDS_32: return m <= 16 && k % kUnitK == 0 && n % 32 == 0;
+    case ALGO_DECODE_LDS_32: return m <= 64 && k % kUnitK == 0 && n % 32 == 0;
     default: return false;
   }
 }
@@ -1609,21 +1613,30 @@ bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
 // The built-in choice: up to 16 rows the unit decode kernel when K allows
 // (32 weight rows per workgroup for several activation rows and N >= 6144,
 // where the activation traffic it halves costs more than the workgroups it
-// gives up), else the register-streaming decode kernel; above 16 rows the
-// largest tile that still gives at least 256 (128, 64) or 512 (256) tiles;
-// for 256 x 256 the pipelined kernel from K = 6144 on (measured crossover:
-// 7% slower than the 8-wavefront kernel at K = 4096, 6% faster at K = 14336).
+// gives up), else the register-streaming decode kernel; 17..64 rows and
+// above as explained at each rule.
 int linear_default_algo(int64_t m, int64_t n, int64_t k) {
   if (m <= 16) {
     if (m >= 2 && n >= 6144 && linear_algo_supported(ALGO_DECODE_LDS_32, m, n, k)) return ALGO_DECODE_LDS_32;
     return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
+  }
+  const int64_t cus = device_cus();
+  // 17..64 rows: the unit decode kernels over 16-row activation blocks (the
+  // weight block is read once per block, mostly from L2), unless above 32
+  // rows the 64x64 tiles alone cover about 3/4 of the CUs: then the tiled
+  // kernel, which reads the weight once, is as fast (measured on the Llama
+  // shapes: decode 2-3x faster at N = 4096 / 6144 and at K = 14336, the
+  // tiled kernels 10-25% faster at N = 14336, K = 4096, M >= 48)
+  if (m <= 64 && linear_algo_supported(ALGO_DECODE_LDS, m, n, k) && !(m > 32 && 4 * ((n + 63) / 64) >= 3 * cus)) {
+    if ((m > 24 || n >= 14336 || k >= 8192) && linear_algo_supported(ALGO_DECODE_LDS_32, m, n, k))
+      return ALGO_DECODE_LDS_32;
+    return ALGO_DECODE_LDS;
   }
   // Rounds of tiles over the CUs: one 256x256 tile per CU at a time, two
   // 128x128 ones.  A 128x128 round takes about 0.65 of a 256x256 one
   // (measured on the Llama shapes at M = 1024..4096), so the 256x256
   // configuration wins once it needs at most 2/3 as many rounds, and always
   // from two full rounds on.
-  const int64_t cus = device_cus();
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
   const int64_t r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);

@@ -168,7 +168,8 @@ def test_linear_algos(lib):
                      b"wide_256x256", b"decode_lds_32"]
     assert lib.sfr_linear_algo_name(7) is None and lib.sfr_linear_algo_name(-1) is None
     sup = lambda a, m, n, k: lib.sfr_linear_algo_supported(a, m, n, k)
-    assert sup(0, 16, 4096, 4096) == 1 and sup(0, 17, 4096, 4096) == 0      # decode: m <= 16
+    assert sup(0, 64, 4096, 4096) == 1 and sup(0, 65, 4096, 4096) == 0      # unit decode: m <= 64
+    assert sup(6, 64, 4096, 4096) == 1 and sup(6, 65, 4096, 4096) == 0
     assert sup(0, 4, 4096, 640) == 0 and sup(0, 4, 4096, 17408) == 1        # unit decode: k % 1024, any K
     assert sup(6, 4, 4096, 1024) == 1 and sup(6, 4, 4112, 1024) == 0        # 32 rows per workgroup: n % 32
     assert sup(1, 16, 4096, 640) == 1 and sup(1, 17, 4096, 640) == 0
@@ -185,6 +186,11 @@ def test_linear_algos(lib):
     # 256x256 tiles from 2/3 of the 128x128 configuration's rounds (256 CUs without a GPU)
     assert d(1024, 14336, 4096) == 4 and d(2048, 4096, 4096) == 3 and d(4096, 4096, 14336) == 4
     assert d(2048, 4096, 14336) == 3 and d(1024, 6144, 4096) == 3
+    # 17..64 rows: unit decode over 16-row blocks, except above 32 rows when
+    # the 64x64 tiles cover about 3/4 of the CUs
+    assert d(17, 4096, 4096) == 0 and d(32, 4096, 4096) == 6 and d(64, 6144, 4096) == 6
+    assert d(17, 14336, 4096) == 6 and d(48, 14336, 4096) == 2 and d(64, 4096, 14336) == 6
+    assert d(64, 4096, 640) == 2 and d(65, 4096, 4096) == 2
 
 
 def test_linear_algo_validation(lib):

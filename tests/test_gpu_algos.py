@@ -29,7 +29,10 @@ SHAPES = [("all_algos", 7, 1040, 1024, E4, E4, True), ("tiled", 300, 4112, 640, 
           ("one_step", 300, 528, 128, E4, E4, True), ("two_steps", 260, 1040, 256, E5, E5, False),
           # few tiles and a long K: the four-stage forms of tiled_64x64 and
           # tiled_128x128; 65 k steps, so the last metadata block is partial
-          ("deep_pipeline", 200, 1040, 8320, E5, E4, True)]
+          ("deep_pipeline", 200, 1040, 8320, E5, E4, True),
+          # the unit decode kernels over 16-row activation blocks: 4 blocks,
+          # the last with 2 rows
+          ("decode_column_blocks", 50, 1056, 2048, E4, E5, True)]
 
 
 @pytest.fixture(scope="module", autouse=True)
