@@ -69,7 +69,8 @@ def test_tensorwise_quantize_deterministic(gpu):
 
 
 # (name, m, n, k): decode, tiled, persistent 256x256 (ragged in m and n)
-LINEAR_SHAPES = [("decode1", 1, 4096, 4096), ("decode16", 16, 4096, 4096), ("tiled", 100, 1040, 384),
+LINEAR_SHAPES = [("decode1", 1, 4096, 4096), ("decode16", 16, 4096, 4096), ("decode_blocks", 40, 4096, 2048),
+                 ("tiled", 100, 1040, 384),
                  ("persistent", 4100, 8208, 512)]
 KINDS = [("tensor", "row"), ("row", "tensor"), ("tensor", "tensor")]
 
