@@ -115,8 +115,8 @@ def calibrate_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer shards without communication along N; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus}: multi-GPU runs are not implemented "
+              "(the layer would shard along N, with no communication)", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:
