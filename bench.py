@@ -9,7 +9,7 @@ weight is; its cost is timed separately and reported as ``weight_prep_ms``.
 Workload (headline): Llama-3.1-8B MLP up-projection at prefill,
 M=8192 tokens, K=4096, N=14336, e4m3 x e4m3, bf16 output, synthetic seeded
 inputs.  ``value`` is dense-equivalent TFLOP/s (2*M*N*K per step).  The
-decode-shaped secondary metric (GB/s at M in {1,4,16}, K=N=4096, bf16 bias)
+decode-shaped secondary metric (GB/s at M in {1,4,16}, and batched decode at M in {32,64}; K=N=4096, bf16 bias)
 is reported under ``decode``; those calls rotate over enough distinct weight
 buffers (> 2x the 256 MB last-level cache) that every call reads HBM.
 
@@ -366,7 +366,7 @@ def bench_algo_search():
 
 
 def bench_decode(torch, sfr, sfr_inputs, lib, dev, stream):
-    """GEMM GB/s at M in {1,4,16}, K=N=4096, bf16 bias, rotating weights (> 512 MB);
+    """GEMM GB/s at M in {1,4,16} (and 32, 64: batched decode), K=N=4096, bf16 bias, rotating weights (> 512 MB);
     per-call times from a HIP graph of the calls (the eager loop's rate too)."""
     from sparse_fp8_row_amd import tune
     res = {}

@@ -62,8 +62,9 @@ def smoke_case() -> Case:
 
 
 def decode_cases():
-    """Decode-shaped: M in {1,4,16}, K=N=4096, e4m3 x e4m3, bf16 bias ~N(0,0.01)."""
-    return [Case("decode", 2, m, 4096, 4096, bias=True) for m in (1, 4, 16)]
+    """Decode-shaped: M in {1,4,16} and batched decode M in {32,64}, K=N=4096,
+    e4m3 x e4m3, bf16 bias ~N(0,0.01)."""
+    return [Case("decode", 2, m, 4096, 4096, bias=True) for m in (1, 4, 16, 32, 64)]
 
 
 def prefill_up_case() -> Case:
