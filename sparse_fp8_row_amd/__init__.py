@@ -36,7 +36,8 @@ STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN"
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
 EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
             "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
-            "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count",
+            "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_rowwise_linear_dynamic_algo",
+            "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count", "sfr_linear_algo_valid",
             "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
             "bsr_count_bf16", "bsr_fill_bf16", "bsr_linear_bf16", "sfr_status_string", "sfr_format_version")
 
@@ -65,6 +66,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
     lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
     lib.sparse_fp8_rowwise_linear_dynamic.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, P]
+    lib.sparse_fp8_rowwise_linear_dynamic_algo.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, I, P]
+    lib.sfr_linear_algo_valid.argtypes = [I]
+    lib.sfr_linear_algo_valid.restype = I
     lib.sparse_fp8_scaled_linear_algo.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, I, P]
     lib.sparse_fp8_scaled_linear_algo.restype = I
     lib.sfr_linear_algo_count.argtypes = []
@@ -80,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsr_linear_bf16.argtypes = [P, I64, I64, P, P, P, I64, P, P, I, P]
     for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
                lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic,
+               lib.sparse_fp8_rowwise_linear_dynamic_algo,
                lib.bsr_count_bf16, lib.bsr_fill_bf16, lib.bsr_linear_bf16):
         fn.restype = I
     lib.sfr_quantize_tensorwise_workspace_bytes.argtypes = [I64, I64]
@@ -157,6 +162,10 @@ def compress_2to4_fp8(wq: torch.Tensor, stream=None):
 
 
 SFR_ALGO_DEFAULT = -1
+# Flag of an algorithm id: FP8 matrix-instruction accumulation (twice the
+# instruction rate; the products of one 128-k step are added 13 bits below
+# the largest).  Without it the accumulation is binary32-grade.
+SFR_ALGO_ACC_F8 = 0x100
 # Algorithm table consulted by sparse_fp8_scaled_linear when no algo is given:
 # {(m_bucket, n, k): algo}, filled by set_algo_table (see tune.py).
 _algo_table = {}
@@ -171,10 +180,19 @@ def m_bucket(m: int) -> int:
     return M_BUCKETS[-1]
 
 
-def linear_algos():
-    """[(id, name)] of the linear layer's kernel configurations."""
+def linear_algos(acc: Optional[str] = None):
+    """[(id, name)] of the linear layer's algorithms: every kernel
+    configuration with binary32-grade accumulation (acc="f32"), with FP8
+    matrix-instruction accumulation (acc="f8"), or both (None)."""
     lib = load()
-    return [(i, lib.sfr_linear_algo_name(i).decode()) for i in range(lib.sfr_linear_algo_count())]
+    flags = {"f32": (0,), "f8": (SFR_ALGO_ACC_F8,), None: (0, SFR_ALGO_ACC_F8)}[acc]
+    ids = [i | f for f in flags for i in range(lib.sfr_linear_algo_count())]
+    return [(a, lib.sfr_linear_algo_name(a).decode()) for a in ids if lib.sfr_linear_algo_valid(a)]
+
+
+def algo_acc(algo: int) -> str:
+    """Accumulation of an algorithm id: "f8" or "f32"."""
+    return "f8" if algo >= 0 and algo & SFR_ALGO_ACC_F8 else "f32"
 
 
 def algo_supported(algo: int, m: int, n: int, k: int) -> bool:
@@ -267,7 +285,8 @@ def sparse_fp8_rowwise_linear(xq: torch.Tensor, xs: torch.Tensor, values: torch.
 
 def sparse_fp8_rowwise_linear_dynamic(x: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, ws: torch.Tensor,
                                       bias: Optional[torch.Tensor] = None, act_dtype=torch.float8_e4m3fn,
-                                      out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+                                      out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None,
+                                      algo: Optional[int] = None):
     """bf16 x [m, k] -> (out [m, n], xq [m, k], xs [m]): row-wise activation
     quantization and the linear layer, fused into one launch for small decode shapes."""
     for t, nm in ((x, "x"), (values, "values"), (meta, "meta"), (ws, "ws")):
@@ -292,10 +311,11 @@ def sparse_fp8_rowwise_linear_dynamic(x: torch.Tensor, values: torch.Tensor, met
         raise ValueError("out has the wrong shape or dtype")
     xq = torch.empty((m, k), dtype=act_dtype, device=x.device)
     xs = torch.empty((m,), dtype=torch.float32, device=x.device)
-    _check(load().sparse_fp8_rowwise_linear_dynamic(
+    _check(load().sparse_fp8_rowwise_linear_dynamic_algo(
         x.data_ptr(), _fp8_enum(act_dtype), m, k, values.data_ptr(), meta.data_ptr(), _fp8_enum(values.dtype),
         ws.data_ptr(), wk, n, 0 if bias is None else bias.data_ptr(), out.data_ptr(), od, xq.data_ptr(),
-        xs.data_ptr(), _stream(stream)), "sparse_fp8_rowwise_linear_dynamic")
+        xs.data_ptr(), SFR_ALGO_DEFAULT if algo is None else int(algo), _stream(stream)),
+        "sparse_fp8_rowwise_linear_dynamic")
     return out, xq, xs
 
 

@@ -64,6 +64,8 @@ sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t d
 
 int sfr_linear_algo_count(void) { return sfr::ALGO_COUNT; }
 
+int sfr_linear_algo_valid(int algo) { return sfr::linear_algo_valid(algo) ? 1 : 0; }
+
 const char* sfr_linear_algo_name(int algo) { return sfr::linear_algo_name(algo); }
 
 int sfr_linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
@@ -79,7 +81,7 @@ sfr_status sparse_fp8_scaled_linear_algo(const uint8_t* xq, sfr_fp8_t x_dt, cons
                                          const uint16_t* bias, void* out, sfr_out_t out_dt, int algo,
                                          void* stream) {
   if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32) || !scale_ok(xs_kind) ||
-      !scale_ok(ws_kind) || algo < SFR_ALGO_DEFAULT || algo >= sfr::ALGO_COUNT)
+      !scale_ok(ws_kind) || (algo != SFR_ALGO_DEFAULT && !sfr::linear_algo_valid(algo)))
     return SFR_ERR_DTYPE;
   if (m < 0 || m > SFR_MAX_DIM || n < 0 || n > SFR_MAX_DIM || n % 16 != 0 || k <= 0 || k > SFR_MAX_DIM ||
       k % 128 != 0 || m * k > kMaxElems || n * k > kMaxElems || m * n > kMaxElems)
@@ -103,24 +105,34 @@ sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const flo
                                        out_dt, SFR_ALGO_DEFAULT, stream);
 }
 
-sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, int64_t m, int64_t k,
-                                             const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
-                                             const float* ws, sfr_scale_t ws_kind, int64_t n, const uint16_t* bias,
-                                             void* out, sfr_out_t out_dt, uint8_t* xq, float* xs,
-                                             void* stream) {
-  if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32) || !scale_ok(ws_kind))
+sfr_status sparse_fp8_rowwise_linear_dynamic_algo(const uint16_t* x, sfr_fp8_t x_dt, int64_t m, int64_t k,
+                                                  const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                                  const float* ws, sfr_scale_t ws_kind, int64_t n,
+                                                  const uint16_t* bias, void* out, sfr_out_t out_dt, uint8_t* xq,
+                                                  float* xs, int algo, void* stream) {
+  if (!fp8_ok(x_dt) || !fp8_ok(w_dt) || (out_dt != SFR_OUT_BF16 && out_dt != SFR_OUT_F32) || !scale_ok(ws_kind) ||
+      (algo != SFR_ALGO_DEFAULT && !sfr::linear_algo_valid(algo)))
     return SFR_ERR_DTYPE;
   if (m < 0 || m > SFR_MAX_DIM || n < 0 || n > SFR_MAX_DIM || n % 16 != 0 || k <= 0 || k > SFR_MAX_DIM ||
       k % 128 != 0 || m * k > kMaxElems || n * k > kMaxElems || m * n > kMaxElems)
     return SFR_ERR_SHAPE;
   if (m == 0 || n == 0) return SFR_OK;
+  if (algo != SFR_ALGO_DEFAULT && !sfr::linear_algo_supported(algo, m, n, k)) return SFR_ERR_SHAPE;
   if (!x || !values || !meta || !ws || !out || !xq || !xs) return SFR_ERR_NULL;
   if (!aligned16(x) || !aligned16(values) || !aligned16(meta) || !aligned16(ws) || !aligned16(out) ||
       !aligned16(xq) || !aligned16(xs) || (bias && !aligned16(bias)))
     return SFR_ERR_ALIGN;
   sfr::LinearArgs a{xq, xs, values, meta, ws, bias, out, m, n, k, (int)x_dt, (int)w_dt, (int)out_dt, 1,
                     ws_kind == SFR_SCALE_ROW ? 1 : 0};
-  return launch_status(sfr::launch_linear_dynamic(x, xq, xs, a, static_cast<hipStream_t>(stream)));
+  return launch_status(sfr::launch_linear_dynamic(x, xq, xs, a, algo, static_cast<hipStream_t>(stream)));
+}
+
+sfr_status sparse_fp8_rowwise_linear_dynamic(const uint16_t* x, sfr_fp8_t x_dt, int64_t m, int64_t k,
+                                             const uint8_t* values, const uint8_t* meta, sfr_fp8_t w_dt,
+                                             const float* ws, sfr_scale_t ws_kind, int64_t n, const uint16_t* bias,
+                                             void* out, sfr_out_t out_dt, uint8_t* xq, float* xs, void* stream) {
+  return sparse_fp8_rowwise_linear_dynamic_algo(x, x_dt, m, k, values, meta, w_dt, ws, ws_kind, n, bias, out, out_dt,
+                                                xq, xs, SFR_ALGO_DEFAULT, stream);
 }
 
 sfr_status sparse_fp8_rowwise_linear(const uint8_t* xq, sfr_fp8_t x_dt, const float* xs, int64_t m, int64_t k,

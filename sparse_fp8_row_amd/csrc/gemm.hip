@@ -323,7 +323,8 @@ struct StageLoader {
   }
 };
 
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC, int MB, int NT>
+template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD, int OCC, int MB, int NT,
+          int ACC>
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -420,7 +421,34 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
     const int mo = MB ? 16 * ((kt % (MB ? MB : 1)) ^ (r16 & 7)) + ((kt / (MB ? MB : 1)) & 1) * C::META_BLOCK -
                             (int)(base - smem)
                       : 0;
-    if constexpr (ORD == 0) {
+    if constexpr (ACC == ACC_F32) {
+      // binary32-grade accumulation: every weight fragment widened once per
+      // step (both halves), then one activation block at a time, each half
+      // widened once and fed to the FN instructions of that half
+      v4i aw[2][C::FN];
+      int ix[2][C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const v4i a = *reinterpret_cast<const v4i*>(base + a_off[fn]);
+        const int idx = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
+        aw[0][fn] = widen_a_half<WF, 0>(a);
+        aw[1][fn] = widen_a_half<WF, 1>(a);
+        ix[0][fn] = idx_half<0>(idx);
+        ix[1][fn] = idx_half<1>(idx);
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+        const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v8i b0 = widen_b_half<XF, 0>(b);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[0][fn], b0, acc[fn][fm], ix[0][fn]);
+        const v8i b1 = widen_b_half<XF, 1>(b);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[1][fn], b1, acc[fn][fm], ix[1][fn]);
+      }
+    } else if constexpr (ORD == 0) {
       // all weight operands of the wavefront tile, then one activation block at
       // a time: each 32-byte B fragment feeds FN instructions
       v4i a[C::FN];
@@ -556,12 +584,15 @@ struct TileBufferLoader {
   }
 };
 
-// NT = 1: output stores are non-temporal.
-template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
+// NT = 1: output stores are non-temporal.  OUT_F32: every wavefront stores
+// its own binary32 block straight from its accumulators (the diagnostic
+// output; the loader wavefronts then also wait for their stores).
+template <int XF, int WF, int OUT, int ACC, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
 __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
+    void* __restrict__ out_, int M, int N, int K, int tiles_m, int tiles_n, int xs_stride, int ws_stride) {
+  uint16_t* const out = reinterpret_cast<uint16_t*>(out_);
   constexpr int S = 2, MB = 8;
   using C = Tiled<BN, BM, WN, WM, S, MB>;
   using L = TileBufferLoader<BN, BM, NL>;
@@ -647,6 +678,38 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
       }
       const uint8_t* base = smem + (kt % S) * C::STAGE;
       const int mo = 16 * ((kt % MB) ^ (r16 & 7)) + ((kt / MB) & 1) * C::META_BLOCK - (int)(base - smem);
+      if constexpr (ACC == ACC_F32) {
+        // as in the tiled kernel: weight fragments widened once per step,
+        // activation blocks one at a time, each half widened once
+        v4i aw[2][C::FN];
+        int ix[2][C::FN];
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const v4i a = *reinterpret_cast<const v4i*>(base + a_off[fn]);
+          const int idx = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
+          aw[0][fn] = widen_a_half<WF, 0>(a);
+          aw[1][fn] = widen_a_half<WF, 1>(a);
+          ix[0][fn] = idx_half<0>(idx);
+          ix[1][fn] = idx_half<1>(idx);
+        }
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+          const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+          const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+          const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const v8i b0 = widen_b_half<XF, 0>(b);
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[0][fn], b0, acc[fn][fm], ix[0][fn]);
+          __builtin_amdgcn_s_setprio(0);
+          const v8i b1 = widen_b_half<XF, 1>(b);
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[1][fn], b1, acc[fn][fm], ix[1][fn]);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        continue;
+      }
       v8i b[C::FM];
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
@@ -676,6 +739,19 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
     int nn0 = 0, nm0 = 0;
     const bool next = tile_of(it + 1, nn0, nm0);
     const int mb = m0 + wm * C::TM, nb = n0 + wn * C::TN;
+    if constexpr (OUT == OUT_F32) {
+      lds_barrier();  // every wavefront is done with the last step's LDS reads
+      if (next && loader_wave) {
+        const L nl(xq, values, meta, M, N, K, nm0, nn0, lw, lane);
+        nl.metablock(meta_lds, 0, KT);
+        nl.stage(smem, 0);
+      }
+      store_tile<OUT_F32>(acc, xs, ws, bias, out_, M, N, mb, nb, r16, lg, xs_stride, ws_stride);
+      if (!next) break;
+      n0 = nn0;
+      m0 = nm0;
+      continue;
+    }
     float xsv[C::FM];
     v4f wsv[C::FN];
     uint2 bv[C::FN];
@@ -975,7 +1051,7 @@ hipError_t run_wide(const LinearArgs& a, hipStream_t stream) {
 // them per pass).  All of a pass's loads are issued before its first MFMA and
 // nothing in between branches, so a wavefront has U * 4 loads in flight.
 // Steps past the end re-read the last step (in bounds) and add a zero A operand.
-template <int XF, int WF, int OUT, int NWV, int U, bool NT = true>
+template <int XF, int WF, int OUT, int ACC, int NWV, int U, bool NT = true>
 __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -1032,7 +1108,7 @@ __global__ __launch_bounds__(64 * NWV) void linear_decode_kernel(
       const v4i av = live ? a[u] : z4;
       const v4i lo = xon ? blo[u] : z4, hi = xon ? bhi[u] : z4;
       const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = smfmac16<XF, WF>(av, b, acc, idx[u]);
+      acc = mma_step<XF, WF, ACC>(av, b, acc, idx[u]);
     }
   }
   red[wave][lane] = acc;
@@ -1074,19 +1150,19 @@ __device__ __forceinline__ void row_bcast_steps(v8i (&b)[8], const v4i& x, std::
 // One unit's 8 MFMA steps for a single activation row: step S's operand is
 // broadcast from x1 (row_bcast_pair<S>) just before its MFMA, so only one
 // step's operand is live at a time.
-template <int XF, int WF, int S>
+template <int XF, int WF, int ACC, int S>
 __device__ __forceinline__ void x1_step(v4f& acc0, v4f& acc1, const v4i& x1, const uint8_t* region, uint32_t a_even,
                                         uint32_t a_odd, uint32_t i_row, int r7) {
   const v4i a = *reinterpret_cast<const v4i*>(region + ((S & 1) ? a_odd : a_even) + 128 * (S >> 1));
   const int idx = *reinterpret_cast<const int*>(region + i_row + 16 * (S ^ r7));
   const v8i b = row_bcast_pair<S>(x1);
-  if constexpr (S & 1) acc1 = smfmac16<XF, WF>(a, b, acc1, idx);
-  else acc0 = smfmac16<XF, WF>(a, b, acc0, idx);
+  if constexpr (S & 1) acc1 = mma_step<XF, WF, ACC>(a, b, acc1, idx);
+  else acc0 = mma_step<XF, WF, ACC>(a, b, acc0, idx);
 }
-template <int XF, int WF, int... S>
+template <int XF, int WF, int ACC, int... S>
 __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, const uint8_t* region, uint32_t a_even,
                                         uint32_t a_odd, uint32_t i_row, int r7, std::integer_sequence<int, S...>) {
-  (x1_step<XF, WF, S>(acc0, acc1, x1, region, a_even, a_odd, i_row, r7), ...);
+  (x1_step<XF, WF, ACC, S>(acc0, acc1, x1, region, a_even, a_odd, i_row, r7), ...);
 }
 
 // Decode kernel, one k unit per wavefront.  A workgroup owns RT * 16 weight
@@ -1106,7 +1182,7 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 // all of the activation) at half the workgroups.
 constexpr int kUnitK = 1024;
 constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
-template <int XF, int WF, int OUT, int RT, bool X1>
+template <int XF, int WF, int OUT, int ACC, int RT, bool X1>
 __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -1199,8 +1275,8 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
         const uint8_t* rt = region + t * kUnitLds;
         const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
         const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
-        if (s & 1) acc1[t] = smfmac16<XF, WF>(a, b[s], acc1[t], idx);
-        else acc0[t] = smfmac16<XF, WF>(a, b[s], acc0[t], idx);
+        if (s & 1) acc1[t] = mma_step<XF, WF, ACC>(a, b[s], acc1[t], idx);
+        else acc0[t] = mma_step<XF, WF, ACC>(a, b[s], acc0[t], idx);
       }
     }
     // the region's reads are complete (their values fed the MFMAs) before
@@ -1236,14 +1312,14 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-template <int XF, int WF, int OUT, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1, int MB = 0,
-          int NT = 0>
+template <int XF, int WF, int OUT, int ACC, int BN, int BM, int WN, int WM, int G, int S, int ORD = 0, int OCC = 1,
+          int MB = 0, int NT = 0>
 hipError_t run_tiled(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, S, MB>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   const int grid = 8 * ((T + 7) / 8);
-  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC, MB, NT>;
+  auto kern = linear_tiled_kernel<XF, WF, OUT, BN, BM, WN, WM, G, S, ORD, OCC, MB, NT, ACC>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1279,14 +1355,14 @@ inline bool tiled_deep(const LinearArgs& a, int tile, int per_cu, int64_t min_k)
   return a.k >= min_k && tiles <= (int64_t)per_cu * device_cus();
 }
 
-template <int XF, int WF, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
+template <int XF, int WF, int OUT, int ACC, int BN, int BM, int WN, int WM, int NL, int G, int OCC, int NT = 0>
 hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
   using C = Tiled<BN, BM, WN, WM, 2, 8>;
   const int tiles_m = (int)((a.m + BM - 1) / BM), tiles_n = (int)((a.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
   // a multiple of 8 workgroups (the XCD mapping), at most OCC per CU
   const int grid = std::max(8, std::min(8 * ((T + 7) / 8), (OCC * device_cus() / 8) * 8));
-  auto kern = linear_persistent_kernel<XF, WF, BN, BM, WN, WM, NL, G, OCC, NT>;
+  auto kern = linear_persistent_kernel<XF, WF, OUT, ACC, BN, BM, WN, WM, NL, G, OCC, NT>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1294,9 +1370,8 @@ hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws, a.bias,
-                     reinterpret_cast<uint16_t*>(a.out), (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride,
-                     a.ws_stride);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, a.xq, a.xs, a.values, a.meta, a.ws, a.bias, a.out,
+                     (int)a.m, (int)a.n, (int)a.k, tiles_m, tiles_n, a.xs_stride, a.ws_stride);
   return hipGetLastError();
 }
 
@@ -1307,9 +1382,9 @@ inline int unit_waves(int64_t k) {
   return (nu + per - 1) / per;
 }
 
-template <int XF, int WF, int OUT, int RT, bool X1>
+template <int XF, int WF, int OUT, int ACC, int RT, bool X1>
 hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
-  auto kern = linear_decode_unit_kernel<XF, WF, OUT, RT, X1>;
+  auto kern = linear_decode_unit_kernel<XF, WF, OUT, ACC, RT, X1>;
   const int nw = unit_waves(a.k);
   const unsigned lds = (unsigned)(nw * RT * kUnitLds);
   static bool attr_set = false;  // benign race: every thread sets the same value
@@ -1325,10 +1400,10 @@ hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int XF, int WF, int OUT, int RT>
+template <int XF, int WF, int OUT, int ACC, int RT>
 hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
-  if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, RT, true>(a, stream);
-  return run_decode_unit_cfg<XF, WF, OUT, RT, false>(a, stream);
+  if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, true>(a, stream);
+  return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, false>(a, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -1384,7 +1459,7 @@ __device__ __forceinline__ void fused_first_loads(uint8_t* __restrict__ xl, uint
     for (int h = 0; h < 2; ++h) xa[c][h] = reinterpret_cast<const uint4*>(xl + (2 * c + h) * 1024)[lane];
 }
 
-template <int XF, int WF, int OUT, int NWMAX>
+template <int XF, int WF, int OUT, int ACC, int NWMAX>
 __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_unit_fused1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
     const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const float* __restrict__ ws,
@@ -1485,7 +1560,7 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
         dma(wave + c * NW);
       }
       wait_vmcnt<0>();
-      x1_unit<XF, WF>(acc0, acc1, x1[c], region, a_even, a_odd, i_row, r7, std::make_integer_sequence<int, 8>{});
+      x1_unit<XF, WF, ACC>(acc0, acc1, x1[c], region, a_even, a_odd, i_row, r7, std::make_integer_sequence<int, 8>{});
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -1514,11 +1589,11 @@ inline bool fused_decode_ok(int64_t m, int64_t k) {
   return m == 1 && k % kUnitK == 0 && k <= 8 * kFusedMaxUnitsPerWave * kUnitK;
 }
 
-template <int XF, int WF, int OUT, int NWMAX>
+template <int XF, int WF, int OUT, int ACC, int NWMAX>
 hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int nw,
                                hipStream_t stream) {
   constexpr unsigned lds = NWMAX * kUnitLds + NWMAX * (NWMAX == 8 ? kFusedMaxUnitsPerWave : 1) * 2048 + 4 * NWMAX;
-  auto kern = linear_decode_unit_fused1_kernel<XF, WF, OUT, NWMAX>;
+  auto kern = linear_decode_unit_fused1_kernel<XF, WF, OUT, ACC, NWMAX>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1531,22 +1606,22 @@ hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const 
   return hipGetLastError();
 }
 
-template <int XF, int WF, int OUT>
+template <int XF, int WF, int OUT, int ACC>
 hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
   // the static LDS is sized for the smallest of 2, 4, 8 wavefronts that covers
   // the units, so small K keeps several workgroups per CU
   const int nw = unit_waves(a.k);
-  if (nw <= 2) return run_decode_fused_nw<XF, WF, OUT, 2>(x, xq, xs, a, nw, stream);
-  if (nw <= 4) return run_decode_fused_nw<XF, WF, OUT, 4>(x, xq, xs, a, nw, stream);
-  return run_decode_fused_nw<XF, WF, OUT, 8>(x, xq, xs, a, nw, stream);
+  if (nw <= 2) return run_decode_fused_nw<XF, WF, OUT, ACC, 2>(x, xq, xs, a, nw, stream);
+  if (nw <= 4) return run_decode_fused_nw<XF, WF, OUT, ACC, 4>(x, xq, xs, a, nw, stream);
+  return run_decode_fused_nw<XF, WF, OUT, ACC, 8>(x, xq, xs, a, nw, stream);
 }
 
-template <int XF, int WF, int OUT>
+template <int XF, int WF, int OUT, int ACC>
 hipError_t run_decode_reg(const LinearArgs& a, hipStream_t stream) {
   const int64_t kt = a.k / KSTEP;
   const dim3 grid((unsigned)(a.n / 16));
 #define SFR_DEC(NWV, U)                                                                                      \
-  hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT, NWV, U>), grid, dim3(64 * NWV), 0, stream, a.xq, a.xs, \
+  hipLaunchKernelGGL((linear_decode_kernel<XF, WF, OUT, ACC, NWV, U>), grid, dim3(64 * NWV), 0, stream, a.xq, a.xs, \
                      a.values, a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride)
   if (kt <= 8) SFR_DEC(8, 1);
   else if (kt <= 16) SFR_DEC(8, 2);
@@ -1558,64 +1633,79 @@ hipError_t run_decode_reg(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int XF, int WF, int OUT>
-hipError_t run_algo(const LinearArgs& a, int algo, hipStream_t stream) {
-  switch (algo) {
-    case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, 1>(a, stream);
-    case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT>(a, stream);
+template <int XF, int WF, int OUT, int ACC>
+hipError_t run_algo(const LinearArgs& a, int cfg, hipStream_t stream) {
+  switch (cfg) {
+    case ALGO_DECODE_LDS: return run_decode_unit<XF, WF, OUT, ACC, 1>(a, stream);
+    case ALGO_DECODE_REG: return run_decode_reg<XF, WF, OUT, ACC>(a, stream);
     // Four stages instead of two where few tiles share a CU (one or two
     // workgroups per CU hide little latency by themselves) and K is long
     // enough for the deeper pipeline to pay: each load then has three k steps
     // to land.  Same arithmetic, same order, bit-identical output.
     case ALGO_TILED_64:
-      if (tiled_deep(a, 64, 2, 8192)) return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
-      return run_tiled<XF, WF, OUT, 64, 64, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
+      if (tiled_deep(a, 64, 2, 8192)) return run_tiled<XF, WF, OUT, ACC, 64, 64, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, ACC, 64, 64, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
     case ALGO_TILED_128:
-      if (tiled_deep(a, 128, 1, 4096)) return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
-      return run_tiled<XF, WF, OUT, 128, 128, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
+      if (tiled_deep(a, 128, 1, 4096)) return run_tiled<XF, WF, OUT, ACC, 128, 128, 2, 2, 8, 4, 0, 1, 8, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, ACC, 128, 128, 2, 2, 8, 2, 0, 1, 8, 1>(a, stream);
     case ALGO_TILED_256:
       // non-temporal output stores: the GEMM's speed is the same, and the
       // next kernel's traffic no longer waits behind its dirty lines
-      if (OUT == OUT_BF16 && persistent_ok(a, 256)) return run_persistent<XF, WF, 256, 256, 4, 2, 4, 8, 1, 1>(a, stream);
-      return run_tiled<XF, WF, OUT, 256, 256, 4, 2, 8, 2, 2, 1, 8, 1>(a, stream);
-    case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, 2>(a, stream);
-    default: return run_wide<XF, WF, OUT, 8>(a, stream);  // ALGO_WIDE_256
+      if (persistent_ok(a, 256)) return run_persistent<XF, WF, OUT, ACC, 256, 256, 4, 2, 4, 8, 1, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, ACC, 256, 256, 4, 2, 8, 2, 2, 1, 8, 1>(a, stream);
+    case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, ACC, 2>(a, stream);
+    default:  // ALGO_WIDE_256: FP8 accumulation only (checked by linear_algo_supported)
+      if constexpr (ACC == ACC_F8) return run_wide<XF, WF, OUT, 8>(a, stream);
+      else return hipErrorInvalidValue;
   }
 }
 
 template <int XF, int WF>
-hipError_t run_out(const LinearArgs& a, int algo, hipStream_t stream) {
-  if (a.out_fmt == OUT_BF16) return run_algo<XF, WF, OUT_BF16>(a, algo, stream);
-  return run_algo<XF, WF, OUT_F32>(a, algo, stream);
+hipError_t run_out(const LinearArgs& a, int cfg, int acc, hipStream_t stream) {
+  if (acc == ACC_F8) {
+    if (a.out_fmt == OUT_BF16) return run_algo<XF, WF, OUT_BF16, ACC_F8>(a, cfg, stream);
+    return run_algo<XF, WF, OUT_F32, ACC_F8>(a, cfg, stream);
+  }
+  if (a.out_fmt == OUT_BF16) return run_algo<XF, WF, OUT_BF16, ACC_F32>(a, cfg, stream);
+  return run_algo<XF, WF, OUT_F32, ACC_F32>(a, cfg, stream);
 }
 
 }  // namespace
 
 const char* linear_algo_name(int algo) {
-  static const char* const names[ALGO_COUNT] = {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128",
-                                                "tiled_256x256", "wide_256x256", "decode_lds_32"};
-  return algo >= 0 && algo < ALGO_COUNT ? names[algo] : nullptr;
+  static const char* const names[2][ALGO_COUNT] = {
+      {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128", "tiled_256x256", nullptr, "decode_lds_32"},
+      {"decode_lds+f8acc", "decode_reg+f8acc", "tiled_64x64+f8acc", "tiled_128x128+f8acc", "tiled_256x256+f8acc",
+       "wide_256x256+f8acc", "decode_lds_32+f8acc"}};
+  if (algo < 0 || (algo & ~(ALGO_ACC_F8_FLAG | 0xFF)) != 0) return nullptr;
+  const int cfg = algo & 0xFF;
+  const bool f8 = (algo & ALGO_ACC_F8_FLAG) != 0;
+  if (cfg >= ALGO_COUNT || (cfg == ALGO_WIDE_256 && !f8)) return nullptr;  // FP8 accumulation only
+  return names[f8 ? 1 : 0][cfg];
 }
 
+bool linear_algo_valid(int algo) { return linear_algo_name(algo) != nullptr; }
+
 bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
-  switch (algo) {
+  if (!linear_algo_valid(algo)) return false;
+  switch (algo & 0xFF) {
     case ALGO_DECODE_LDS: return m <= 64 && k % kUnitK == 0;
     case ALGO_DECODE_REG: return m <= 16;
     case ALGO_TILED_64:
     case ALGO_TILED_128:
     case ALGO_TILED_256: return true;
-    case ALGO_WIDE_256: return k >= 4 * KSTEP;
+    case ALGO_WIDE_256: return (algo & ALGO_ACC_F8_FLAG) && k >= 4 * KSTEP;
     case ALGO_DECODE_LDS_32: return m <= 64 && k % kUnitK == 0 && n % 32 == 0;
     default: return false;
   }
 }
 
-// The built-in choice: up to 16 rows the unit decode kernel when K allows
-// (32 weight rows per workgroup for several activation rows and N >= 6144,
-// where the activation traffic it halves costs more than the workgroups it
-// gives up), else the register-streaming decode kernel; 17..64 rows and
-// above as explained at each rule.
-int linear_default_algo(int64_t m, int64_t n, int64_t k) {
+// The built-in kernel configuration: up to 16 rows the unit decode kernel
+// when K allows (32 weight rows per workgroup for several activation rows and
+// N >= 6144, where the activation traffic it halves costs more than the
+// workgroups it gives up), else the register-streaming decode kernel; 17..64
+// rows and above as explained at each rule.
+static int default_config(int64_t m, int64_t n, int64_t k) {
   if (m <= 16) {
     if (m >= 2 && n >= 6144 && linear_algo_supported(ALGO_DECODE_LDS_32, m, n, k)) return ALGO_DECODE_LDS_32;
     return linear_algo_supported(ALGO_DECODE_LDS, m, n, k) ? ALGO_DECODE_LDS : ALGO_DECODE_REG;
@@ -1645,37 +1735,49 @@ int linear_default_algo(int64_t m, int64_t n, int64_t k) {
   return ALGO_TILED_64;
 }
 
+// The built-in choice: binary32-grade accumulation everywhere (the stated
+// accuracy of the layer holds for every input).
+int linear_default_algo(int64_t m, int64_t n, int64_t k) { return default_config(m, n, k); }
+
 hipError_t launch_linear_algo(const LinearArgs& a, int algo, hipStream_t stream) {
   if (algo < 0) algo = linear_default_algo(a.m, a.n, a.k);
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_out<FMT_E4M3, FMT_E4M3>(a, algo, stream);
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_out<FMT_E4M3, FMT_E5M2>(a, algo, stream);
-  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_out<FMT_E5M2, FMT_E4M3>(a, algo, stream);
-  return run_out<FMT_E5M2, FMT_E5M2>(a, algo, stream);
+  const int cfg = algo & 0xFF, acc = (algo & ALGO_ACC_F8_FLAG) ? ACC_F8 : ACC_F32;
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_out<FMT_E4M3, FMT_E4M3>(a, cfg, acc, stream);
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_out<FMT_E4M3, FMT_E5M2>(a, cfg, acc, stream);
+  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_out<FMT_E5M2, FMT_E4M3>(a, cfg, acc, stream);
+  return run_out<FMT_E5M2, FMT_E5M2>(a, cfg, acc, stream);
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) { return launch_linear_algo(a, -1, stream); }
 
 template <int XF, int WF>
-hipError_t run_fused_out(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
-  if (a.out_fmt == OUT_BF16) return run_decode_fused<XF, WF, OUT_BF16>(x, xq, xs, a, stream);
-  return run_decode_fused<XF, WF, OUT_F32>(x, xq, xs, a, stream);
+hipError_t run_fused_out(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int acc, hipStream_t stream) {
+  if (acc == ACC_F8) {
+    if (a.out_fmt == OUT_BF16) return run_decode_fused<XF, WF, OUT_BF16, ACC_F8>(x, xq, xs, a, stream);
+    return run_decode_fused<XF, WF, OUT_F32, ACC_F8>(x, xq, xs, a, stream);
+  }
+  if (a.out_fmt == OUT_BF16) return run_decode_fused<XF, WF, OUT_BF16, ACC_F32>(x, xq, xs, a, stream);
+  return run_decode_fused<XF, WF, OUT_F32, ACC_F32>(x, xq, xs, a, stream);
 }
 
-hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a,
+hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int algo,
                                  hipStream_t stream) {
-  if (!fused_decode_ok(a.m, a.k)) {
+  const int dflt = linear_default_algo(a.m, a.n, a.k);
+  if (algo < 0) algo = dflt;
+  if (!fused_decode_ok(a.m, a.k) || (algo & 0xFF) != (dflt & 0xFF)) {
     // two launches: the row-wise quantization, then the linear layer
     hipError_t e = launch_quantize(x, a.m, a.k, a.x_fmt, xq, xs, stream);
     if (e != hipSuccess) return e;
     LinearArgs b = a;
     b.xq = xq;
     b.xs = xs;
-    return launch_linear(b, stream);
+    return launch_linear_algo(b, algo, stream);
   }
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_fused_out<FMT_E4M3, FMT_E4M3>(x, xq, xs, a, stream);
-  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_fused_out<FMT_E4M3, FMT_E5M2>(x, xq, xs, a, stream);
-  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_fused_out<FMT_E5M2, FMT_E4M3>(x, xq, xs, a, stream);
-  return run_fused_out<FMT_E5M2, FMT_E5M2>(x, xq, xs, a, stream);
+  const int acc = (algo & ALGO_ACC_F8_FLAG) ? ACC_F8 : ACC_F32;
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E4M3) return run_fused_out<FMT_E4M3, FMT_E4M3>(x, xq, xs, a, acc, stream);
+  if (a.x_fmt == FMT_E4M3 && a.w_fmt == FMT_E5M2) return run_fused_out<FMT_E4M3, FMT_E5M2>(x, xq, xs, a, acc, stream);
+  if (a.x_fmt == FMT_E5M2 && a.w_fmt == FMT_E4M3) return run_fused_out<FMT_E5M2, FMT_E4M3>(x, xq, xs, a, acc, stream);
+  return run_fused_out<FMT_E5M2, FMT_E5M2>(x, xq, xs, a, acc, stream);
 }
 
 }  // namespace sfr

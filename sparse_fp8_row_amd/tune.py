@@ -25,8 +25,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import torch
 
-from . import (SFR_E4M3, SFR_E5M2, SFR_OUT_BF16, SFR_SCALE_ROW, _check, _stream, algo_supported, default_algo,
-               linear_algos, load, m_bucket)
+from . import (SFR_ALGO_ACC_F8, SFR_E4M3, SFR_E5M2, SFR_OUT_BF16, SFR_SCALE_ROW, _check, _stream, algo_supported,
+               default_algo, linear_algos, load, m_bucket)
 
 _FMT = {torch.float8_e4m3fn: SFR_E4M3, torch.float8_e5m2: SFR_E5M2}
 
@@ -156,7 +156,11 @@ def search(shapes: Iterable[Tuple[int, int, int]], x_dtype=torch.float8_e4m3fn, 
     names = dict(linear_algos())
     table, records = {}, []
     for m, n, k in shapes:
-        cand = [a for a in (algos if algos is not None else names) if algo_supported(a, m, n, k)]
+        # by default the candidates share the built-in choice's accumulation
+        # (a faster but less accurate choice is never made silently)
+        acc = default_algo(m, n, k) & SFR_ALGO_ACC_F8
+        pool = algos if algos is not None else [a for a in names if a & SFR_ALGO_ACC_F8 == acc]
+        cand = [a for a in pool if algo_supported(a, m, n, k)]
         inp = _Inputs(m, n, k, x_dtype, w_dtype, 600 << 20)
         times = {a: time_algo(m, n, k, a, reps=reps, warmup=warmup, inputs=inp) for a in cand}
         del inp

@@ -11,20 +11,19 @@ Comparison rules (the three the layer's accuracy contract states):
                       exceeds half a bf16 ulp (heavy cancellation), the value
                       is instead held to that tolerance plus half a bf16 ulp;
                       such elements are counted and reported, never skipped.
+Every element must pass: there is no miss budget.  This is the gate of the
+library's default (binary32-grade) accumulation.
 
-Hardware accumulation.  gfx950's FP8 matrix instructions (dense and 2:4
-sparse alike) add the products of one instruction in fixed point aligned to
-the largest of them, keeping 13 fractional bits below its leading bit: a
-product smaller than 2^-13 of the largest is dropped (instruction probe: with
-products 2^16, 2^j, -2^16 the result is 0 for j <= 2 and 2^j for j >= 3).
-Each 128-wide k block of one output therefore carries an error below
-64 * 2^(floor(log2 P) - 13), P the largest product in the block, on top of the
-binary32 rounding.  That bound can exceed 1e-5 * sum|xq*wq| when a short
-dot product cancels heavily, so every element is held to
-1e-5 * sum|xq*wq| + that bound (``hw_bound``), and the elements that miss the
-plain 1e-5 bound are counted and reported as ``strict_misses``; their rate is
-asserted to stay below 1e-3 (measured: none on normal data at K=4096; 2 in
-4.1e6 at K=256; 13 in 1.1e5 on the Student-t/outlier workload at K=14336).
+FP8 matrix-instruction accumulation (algorithm ids with SFR_ALGO_ACC_F8) is
+held to a wider, stated bound instead: gfx950's FP8 matrix instructions add
+the products of one instruction in fixed point 13 bits below the largest of
+them (``test_gpu_accumulation.py`` pins this through the public API: products
+2^16, 2^j, -2^16 in one 128-k step give 2^j for j >= 3 and 0 below).  Each
+128-wide k block of one output therefore carries an error below
+64 * 2^(floor(log2 P) - 13), P the block's largest product, on top of the
+binary32 rounding (``hw_bound``); those algorithms are checked against
+1e-5 * sum|xq*wq| + hw_bound, and the elements that miss the plain bound are
+reported as ``strict_misses``.
 """
 from __future__ import annotations
 
@@ -78,13 +77,13 @@ def bf16_ulp(y: np.ndarray) -> np.ndarray:
     return np.exp2(np.maximum(e, -126) - 7)
 
 
-STRICT_MISS_RATE = 1e-3
 HW_FRAC_BITS = 13
 KBLOCK = 128
 
 
 def hw_bound(xq, xfmt, xs, wdense, wfmt, ws, rows, cols):
-    """Upper bound of the matrix unit's in-instruction truncation, per output.
+    """Upper bound of the FP8 matrix instruction's in-instruction truncation,
+    per output.
 
     For every 128-wide k block: P = max|x| * max|w| over the block bounds the
     largest product; the block's error is below 64 * 2^(floor(log2 P) - 13).
@@ -103,37 +102,49 @@ def hw_bound(xq, xfmt, xs, wdense, wfmt, ws, rows, cols):
     return out * t
 
 
-def check_f32(y_gpu: np.ndarray, ref: dict, has_bias: bool, hwb: np.ndarray) -> dict:
+def check_f32(y_gpu: np.ndarray, ref: dict, has_bias: bool, hwb=None) -> dict:
+    """binary32 output against the oracle: every element within the stated
+    bound (hwb: the FP8-accumulation allowance added to it, or None)."""
     y = ref["y"]
     tol = REL_TOL * ref["sabs"]
     if has_bias:
         tol = tol + np.abs(y) * 2.0**-23
     err = np.abs(y_gpu.astype(np.float64) - y)
     strict = err > tol
-    bad = err > tol + hwb
+    bad = strict if hwb is None else err > tol + hwb
     rel = err / np.maximum(ref["sabs"], 1e-300)
     return {"n": y.size, "bad": int(bad.sum()), "strict_misses": int(strict.sum()),
-            "strict_rate_ok": bool(strict.sum() <= max(1, STRICT_MISS_RATE * y.size)),
             "max_err_over_sabs": float(rel.max(initial=0.0)),
             "first_bad": None if not bad.any() else np.argwhere(bad)[0].tolist()}
 
 
-def check_bf16(bits_gpu: np.ndarray, ref: dict, hwb: np.ndarray) -> dict:
+def check_bf16(bits_gpu: np.ndarray, ref: dict, hwb=None) -> dict:
+    """bf16 output against the oracle: within 1 bf16 ulp, or, where the
+    binary32 tolerance exceeds half an ulp, within that tolerance plus half an
+    ulp (hwb: the FP8-accumulation allowance added to the tolerance, or None)."""
     d = np.abs(ordered(bits_gpu) - ordered(ref["bf16"]))
     y = ref["y"]
     tol32 = REL_TOL * ref["sabs"]
     half = 0.5 * bf16_ulp(y)
-    ill = tol32 + hwb > half
     y_gpu = oracle.bf16_to_float(bits_gpu).astype(np.float64)
     err = np.abs(y_gpu - y)
-    fallback_ok = err <= tol32 + hwb + half
-    bad = (d > 1) & ~(ill & fallback_ok)
-    strict = (d > 1) & ~(err <= tol32 + half)
+    ill = tol32 > half
+    strict = (d > 1) & ~(ill & (err <= tol32 + half))
+    if hwb is None:
+        bad = strict
+        ill_hw = ill
+    else:
+        ill_hw = tol32 + hwb > half
+        bad = (d > 1) & ~(ill_hw & (err <= tol32 + hwb + half))
     return {"n": y.size, "bad": int(bad.sum()), "exact": int((d == 0).sum()), "max_ulp": int(d.max(initial=0)),
             "ill_conditioned": int(ill.sum()), "ill_over_1ulp": int((ill & (d > 1)).sum()),
             "strict_misses": int(strict.sum()),
-            "strict_rate_ok": bool(strict.sum() <= max(1, STRICT_MISS_RATE * y.size)),
             "first_bad": None if not bad.any() else np.argwhere(bad)[0].tolist()}
+
+
+def is_f8_acc(algo) -> bool:
+    """True for an algorithm id with FP8 matrix-instruction accumulation."""
+    return algo is not None and algo >= 0 and bool(algo & 0x100)
 
 
 # Quantization test rows: bf16 bits [rows, cols] of one of four value

@@ -30,6 +30,7 @@ def test_header_declares_the_api():
     for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
               "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
               "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo",
+              "sparse_fp8_rowwise_linear_dynamic_algo", "sfr_linear_algo_valid",
               "sfr_linear_algo_count", "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
               "bsr_count_bf16", "bsr_fill_bf16", "bsr_linear_bf16"):
         assert n in names
@@ -162,19 +163,34 @@ def test_dynamic_linear_validation(lib):
     assert call(x=U) == ALIGN
 
 
+F8 = 0x100   # SFR_ALGO_ACC_F8
+
+
 def test_linear_algos(lib):
     names = [lib.sfr_linear_algo_name(i) for i in range(lib.sfr_linear_algo_count())]
     assert names == [b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128", b"tiled_256x256",
-                     b"wide_256x256", b"decode_lds_32"]
-    assert lib.sfr_linear_algo_name(7) is None and lib.sfr_linear_algo_name(-1) is None
+                     None, b"decode_lds_32"]
+    f8 = [lib.sfr_linear_algo_name(i | F8) for i in range(lib.sfr_linear_algo_count())]
+    assert f8 == [n + b"+f8acc" for n in (b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128",
+                                          b"tiled_256x256", b"wide_256x256", b"decode_lds_32")]
+    for a in (7, -1, 5, 7 | F8, 0x200, 0x300, 1 << 20):
+        assert lib.sfr_linear_algo_name(a) is None and lib.sfr_linear_algo_valid(a) == 0, a
+    assert all(lib.sfr_linear_algo_valid(a) == 1 for a in (0, 4, 6, 0 | F8, 5 | F8, 6 | F8))
     sup = lambda a, m, n, k: lib.sfr_linear_algo_supported(a, m, n, k)
+    # each accumulation supports the same shapes per configuration (the
+    # pipelined kernel only with FP8 accumulation)
+    for a in (0, 1, 2, 3, 4, 6):
+        for shape in ((64, 4096, 4096), (65, 4096, 4096), (4, 4096, 640), (16, 4096, 640), (17, 4096, 640),
+                      (5000, 4096, 256), (4, 4112, 1024)):
+            assert sup(a, *shape) == sup(a | F8, *shape), (a, shape)
+    assert sup(5, 5000, 4096, 512) == 0 and sup(5 | F8, 5000, 4096, 512) == 1   # pipelined: FP8, k >= 512
+    assert sup(5 | F8, 5000, 4096, 384) == 0
     assert sup(0, 64, 4096, 4096) == 1 and sup(0, 65, 4096, 4096) == 0      # unit decode: m <= 64
     assert sup(6, 64, 4096, 4096) == 1 and sup(6, 65, 4096, 4096) == 0
     assert sup(0, 4, 4096, 640) == 0 and sup(0, 4, 4096, 17408) == 1        # unit decode: k % 1024, any K
     assert sup(6, 4, 4096, 1024) == 1 and sup(6, 4, 4112, 1024) == 0        # 32 rows per workgroup: n % 32
     assert sup(1, 16, 4096, 640) == 1 and sup(1, 17, 4096, 640) == 0
     assert all(sup(a, 5000, 4096, 256) == 1 for a in (2, 3, 4))
-    assert sup(5, 5000, 4096, 384) == 0 and sup(5, 5000, 4096, 512) == 1   # pipelined: k >= 512
     assert sup(2, 4, 100, 256) == 0 and sup(7, 4, 128, 256) == 0           # bad n, unknown id
     # the built-in choice
     d = lib.sfr_linear_default_algo
@@ -204,8 +220,11 @@ def test_linear_algo_validation(lib):
                  a["n"], a["bias"], a["out"], a["od"], a["algo"], None)
 
     assert call(algo=7) == DTYPE and call(algo=-2) == DTYPE
+    assert call(algo=5) == DTYPE                  # the pipelined kernel: FP8 accumulation only
+    assert call(algo=0x200) == DTYPE and call(algo=7 | F8) == DTYPE
     assert call(algo=0) == SHAPE                  # k = 256: not a multiple of 1024
-    assert call(algo=5) == SHAPE                  # k < 512
+    assert call(algo=0 | F8) == SHAPE
+    assert call(algo=5 | F8) == SHAPE             # k < 512
     assert call(algo=1, xq=None) == NULL          # supported: validation goes on
     assert call(algo=2, m=0, xq=None, xs=None, out=None) == OK
 

