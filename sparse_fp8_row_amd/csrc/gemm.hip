@@ -679,33 +679,50 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
       const uint8_t* base = smem + (kt % S) * C::STAGE;
       const int mo = 16 * ((kt % MB) ^ (r16 & 7)) + ((kt / MB) & 1) * C::META_BLOCK - (int)(base - smem);
       if constexpr (ACC == ACC_F32) {
-        // as in the tiled kernel: weight fragments widened once per step,
-        // activation blocks one at a time, each half widened once
-        v4i aw[2][C::FN];
-        int ix[2][C::FN];
+        // the step as two half steps (see smfmac16_bf16): per half, the
+        // weight fragments' half widened once, then each activation block's
+        // half (two 8-byte LDS reads) widened once and fed to FN
+        // instructions.  Holding one half at a time keeps registers free for
+        // the LDS reads to run ahead of the matrix instructions.
+        v4i a[C::FN];
+        int idx[C::FN];
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
-          const v4i a = *reinterpret_cast<const v4i*>(base + a_off[fn]);
-          const int idx = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
-          aw[0][fn] = widen_a_half<WF, 0>(a);
-          aw[1][fn] = widen_a_half<WF, 1>(a);
-          ix[0][fn] = idx_half<0>(idx);
-          ix[1][fn] = idx_half<1>(idx);
+          a[fn] = *reinterpret_cast<const v4i*>(base + a_off[fn]);
+          idx[fn] = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
         }
+        // the 2 FM (half, activation block) pairs in order, the activation
+        // halves read PD pairs ahead of their instructions
+        constexpr int NQ = 2 * C::FM, PD = 3;
+        uint2 rlo[NQ], rhi[NQ];
+        auto read_q = [&](int q) __attribute__((always_inline)) {
+          const int h = q / C::FM, fm = q % C::FM;
+          rlo[q] = *reinterpret_cast<const uint2*>(base + b_off0[fm] + 8 * h);
+          rhi[q] = *reinterpret_cast<const uint2*>(base + b_off1[fm] + 8 * h);
+        };
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
-          const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
-          const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const v8i b0 = widen_b_half<XF, 0>(b);
+        for (int q = 0; q < PD; ++q) read_q(q);
+        v4i aw[C::FN];
+        int ix[C::FN];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int h = q / C::FM, fm = q % C::FM;
+          if (q + PD < NQ) read_q(q + PD);
+          if (fm == 0) {
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+              aw[fn] = h ? widen_a_half<WF, 1>(a[fn]) : widen_a_half<WF, 0>(a[fn]);
+              ix[fn] = h ? idx_half<1>(idx[fn]) : idx_half<0>(idx[fn]);
+            }
+          }
+          // widen_b_half<XF, h> of the activation fragment whose half h these are
+          const v8i bw = v8i{widen2<XF, false>((int)rlo[q].x), widen2<XF, true>((int)rlo[q].x),
+                             widen2<XF, false>((int)rlo[q].y), widen2<XF, true>((int)rlo[q].y),
+                             widen2<XF, false>((int)rhi[q].x), widen2<XF, true>((int)rhi[q].x),
+                             widen2<XF, false>((int)rhi[q].y), widen2<XF, true>((int)rhi[q].y)};
           __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[0][fn], b0, acc[fn][fm], ix[0][fn]);
-          __builtin_amdgcn_s_setprio(0);
-          const v8i b1 = widen_b_half<XF, 1>(b);
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[1][fn], b1, acc[fn][fm], ix[1][fn]);
+          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[fn], bw, acc[fn][fm], ix[fn]);
           __builtin_amdgcn_s_setprio(0);
         }
         continue;
