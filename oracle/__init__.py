@@ -79,6 +79,7 @@ def _load():
             "orc_compress_2to4": [P, I64, I64, P, P],
             "orc_decompress_2to4": [P, P, I64, I64, P],
             "orc_prune_2to4": [P, I64, I64, P],
+            "orc_prune_2to4_bf16": [P, I64, I64, P],
             "orc_check_all_groups": [P, P],
             "orc_linear": [P, I, P, I64, I64, P, P, I, P, I64, P, P, I64, P, I64, P, P, P],
             "orc_bsr_fill": [P, I64, I64, I64, P, P, P],
@@ -204,6 +205,29 @@ def prune_2to4(wq: np.ndarray) -> np.ndarray:
     out = np.empty_like(w)
     _load().orc_prune_2to4(_ptr(w), n, k, _ptr(out))
     return out
+
+
+def prune_2to4_bf16(w_bf16: np.ndarray) -> np.ndarray:
+    """2:4 magnitude pruning of bf16 bits [n, k]: in every group of four along
+    k the two largest magnitudes keep their bits (ties to the lower index,
+    +0.0 and -0.0 equal), the other two become +0.0."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    assert k % 4 == 0
+    out = np.empty_like(w)
+    _load().orc_prune_2to4_bf16(_ptr(w), n, k, _ptr(out))
+    return out
+
+
+def prepare_weight(w_bf16: np.ndarray, fmt: int, scaling: str = "row"):
+    """The weight's preparation: 2:4 pruning in bf16, FP8 quantization (one
+    scale per output row, or one for the tensor), compression.
+
+    Returns (values, meta, scale, pruned bf16 bits)."""
+    pruned = prune_2to4_bf16(w_bf16)
+    q, s = (quantize_tensor if scaling == "tensor" else quantize_rows)(pruned, fmt)
+    v, m = compress_2to4(q)
+    return v, m, s, pruned
 
 
 def check_all_groups():

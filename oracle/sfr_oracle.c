@@ -295,6 +295,37 @@ void orc_prune_2to4(const uint8_t* w, int64_t n, int64_t k, uint8_t* out)
     }
 }
 
+/* 2:4 magnitude pruning of a dense bf16 matrix (the weight is pruned before
+ * it is quantized: [P1], the 2:4 sparse weight; a group's two largest
+ * magnitudes survive).  For row r and group g (k = 4g .. 4g+3): position j
+ * survives when fewer than two positions of the group outrank it, where i
+ * outranks j if |w_i| > |w_j|, or |w_i| == |w_j| and i < j (ties go to the
+ * lower index).  Magnitudes are compared as values: +0.0 and -0.0 are both
+ * zero (and tie).  Surviving entries keep their bits; the others become
+ * +0.0.  Finite inputs only. */
+static int bf16_outranks(const uint16_t* g, int i, int j)
+{
+    const double a = fabs((double)orc_bf16_to_float(g[i])), b = fabs((double)orc_bf16_to_float(g[j]));
+    return a > b || (a == b && i < j);
+}
+
+void orc_prune_2to4_bf16(const uint16_t* w, int64_t n, int64_t k, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t g = 0; g < k / 4; ++g) {
+            const uint16_t* gr = w + r * k + 4 * g;
+            uint16_t* o = out + r * k + 4 * g;
+            for (int j = 0; j < 4; ++j) {
+                int above = 0;
+                for (int i = 0; i < 4; ++i)
+                    if (i != j && bf16_outranks(gr, i, j)) ++above;
+                o[j] = above < 2 ? gr[j] : (uint16_t)0x0000;
+            }
+        }
+    }
+}
+
 /* Exhaustive agreement of the two selection formulations over every 4-byte
  * group (2^32 of them).  Returns the number of disagreements, and the number
  * of groups whose chosen pair is not a valid ascending pair. */
