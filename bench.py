@@ -454,8 +454,7 @@ def cpu_baseline(case, rows):
     t_prep = time.perf_counter()
     xb = sfr_inputs.draw_x(case)[:rows]
     wb = sfr_inputs.draw_w(case)
-    wq, ws = oracle.quantize_rows(wb, oracle.E4M3)
-    v, m = oracle.compress_2to4(wq)
+    v, m, ws, _ = oracle.prepare_weight(wb, oracle.E4M3)
     t_prep = time.perf_counter() - t_prep
     t0 = time.perf_counter()
     xq, xs = oracle.quantize_rows(xb, oracle.E4M3)

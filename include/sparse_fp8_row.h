@@ -132,6 +132,7 @@ sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols
  * (at most 4 KB); 0 for sizes it rejects. */
 int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols);
 
+
 /*
  * compress_2to4_fp8 -- 2:4 semi-structured compression of an FP8 matrix.
  * Source: PR #1671 (converter to the 2:4 sparse format; testing found that
@@ -159,6 +160,26 @@ int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols);
  */
 sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t dt,
                              uint8_t* values, uint8_t* meta, void* stream);
+
+/*
+ * prune_2to4_bf16 -- 2:4 magnitude pruning of a bf16 matrix, the weight's
+ * first preparation step (before FP8 quantization and compress_2to4_fp8).
+ * Source: PR #1671 (the weight is 2:4 semi-structured sparse; zeros of
+ * either sign count as zero, the -0.0 issue that PR fixes in the converter).
+ *
+ * For every row and every group of four consecutive k of w ([n, k] bf16
+ * bits), the two entries of largest magnitude keep their bits and the other
+ * two become +0.0 (0x0000); ties go to the lower index and +0.0 / -0.0 have
+ * equal (zero) magnitude.  A row's largest magnitude always survives, so its
+ * row-wise FP8 scale is the same before and after pruning.  Finite inputs
+ * only.  Output is bit-exact and deterministic.
+ *
+ *   w    [n, k] bf16 bits, device, read.
+ *   out  [n, k] bf16 bits, device, written; may be w (in place).
+ * Sizes: 0 <= n <= SFR_MAX_DIM, 0 < k <= SFR_MAX_DIM, k % 8 == 0.
+ * n == 0 is a no-op.
+ */
+sfr_status prune_2to4_bf16(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, void* stream);
 
 /*
  * sparse_fp8_rowwise_linear -- the row-wise scaled linear layer with a 2:4

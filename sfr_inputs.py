@@ -9,8 +9,9 @@ fused qkv 6144) that the pytorch/ao pages run the method on through their
 ``generate.py`` script ("Add CUTLASS-based row-wise scaled sparse FP8 kernel",
 PR #1671, item 5 of the ready-for-review comment).  No weights or prompts of
 that model are used: values are drawn from the distributions listed per
-config below, and the weight is drawn dense; its 2:4 magnitude pruning is the
-method's own step (the compressor), not the generator's.
+config below, and the weight is drawn dense; its 2:4 magnitude pruning (in
+bf16, before quantization) is the method's own first step, not the
+generator's.
 
 Random streams: ``numpy.random.Generator(PCG64(SeedSequence([seed, cfg_id,
 tensor_id])))`` with tensor ids X=0, W=1, bias=2, outlier channels=3,

@@ -35,7 +35,7 @@ SFR_SCALE_ROW, SFR_SCALE_TENSOR = 0, 1
 STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN",
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
 EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
-            "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
+            "compress_2to4_fp8", "prune_2to4_bf16", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
             "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_rowwise_linear_dynamic_algo",
             "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count", "sfr_linear_algo_valid",
             "sfr_linear_algo_name", "sfr_linear_algo_supported", "sfr_linear_default_algo",
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.quantize_rowwise_fp8.argtypes = [P, I64, I64, I, P, P, P]
     lib.compress_2to4_fp8.argtypes = [P, I64, I64, I, P, P, P]
+    lib.prune_2to4_bf16.argtypes = [P, I64, I64, P, P]
     lib.sparse_fp8_rowwise_linear.argtypes = [P, I, P, I64, I64, P, P, I, P, I64, P, P, I, P]
     lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
     lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
@@ -82,7 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsr_count_bf16.argtypes = [P, I64, I64, P, P]
     lib.bsr_fill_bf16.argtypes = [P, I64, I64, P, P, P, P]
     lib.bsr_linear_bf16.argtypes = [P, I64, I64, P, P, P, I64, P, P, I, P]
-    for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.sparse_fp8_rowwise_linear,
+    for fn in (lib.quantize_rowwise_fp8, lib.compress_2to4_fp8, lib.prune_2to4_bf16, lib.sparse_fp8_rowwise_linear,
                lib.quantize_tensorwise_fp8, lib.sparse_fp8_scaled_linear, lib.sparse_fp8_rowwise_linear_dynamic,
                lib.sparse_fp8_rowwise_linear_dynamic_algo,
                lib.bsr_count_bf16, lib.bsr_fill_bf16, lib.bsr_linear_bf16):
@@ -159,6 +160,21 @@ def compress_2to4_fp8(wq: torch.Tensor, stream=None):
     _check(load().compress_2to4_fp8(wq.data_ptr(), n, k, _fp8_enum(wq.dtype), values.data_ptr(),
                                     meta.data_ptr(), _stream(stream)), "compress_2to4_fp8")
     return values, meta
+
+
+def prune_2to4_bf16(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bf16 [n, k] -> the same with each group of four along k pruned to its
+    two largest magnitudes (the others +0.0).  out may be w (in place)."""
+    _dev(w, "w")
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("w must be a 2-D bfloat16 tensor")
+    n, k = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    elif out.shape != w.shape or out.dtype != w.dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(load().prune_2to4_bf16(w.data_ptr(), n, k, out.data_ptr(), _stream(stream)), "prune_2to4_bf16")
+    return out
 
 
 SFR_ALGO_DEFAULT = -1
@@ -329,18 +345,19 @@ class SparseFp8Weight:
 
 
 def prepare_weight(w: torch.Tensor, dtype=torch.float8_e4m3fn, stream=None, scaling: str = "row") -> SparseFp8Weight:
-    """bf16 weight [N, K] -> FP8 quantization (row-wise, or tensor-wise with
-    scaling="tensor"), then 2:4 compression.
+    """bf16 weight [N, K] -> 2:4 magnitude pruning in bf16, FP8 quantization
+    (row-wise, or tensor-wise with scaling="tensor"), 2:4 compression.
 
-    The compressor keeps the two largest FP8 magnitudes of every group of four,
-    which is the 2:4 magnitude pruning; the scale is unaffected by it because
-    a row's largest element is always kept."""
-    if scaling == "row":
-        wq, ws = quantize_rowwise_fp8(w, dtype, stream)
-    elif scaling == "tensor":
-        wq, ws = quantize_tensorwise_fp8(w, dtype, stream)
-    else:
+    The compressor then keeps each group's two survivors; the row scales are
+    those of the dense weight, since a row's largest element always survives."""
+    if scaling not in ("row", "tensor"):
         raise ValueError("scaling must be 'row' or 'tensor'")
+    pruned = prune_2to4_bf16(w, stream=stream)
+    if scaling == "row":
+        wq, ws = quantize_rowwise_fp8(pruned, dtype, stream)
+    else:
+        wq, ws = quantize_tensorwise_fp8(pruned, dtype, stream)
+    del pruned
     values, meta = compress_2to4_fp8(wq, stream)
     return SparseFp8Weight(values, meta, ws, int(load().sfr_format_version()))
 

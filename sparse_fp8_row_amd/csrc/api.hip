@@ -62,6 +62,15 @@ sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t d
   return launch_status(sfr::launch_compress(w, n, k, values, meta, static_cast<hipStream_t>(stream)));
 }
 
+sfr_status prune_2to4_bf16(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, void* stream) {
+  if (n < 0 || n > SFR_MAX_DIM || k <= 0 || k > SFR_MAX_DIM || k % 8 != 0 || n * k > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (n == 0) return SFR_OK;
+  if (!w || !out) return SFR_ERR_NULL;
+  if (!aligned16(w) || !aligned16(out)) return SFR_ERR_ALIGN;
+  return launch_status(sfr::launch_prune_bf16(w, n, k, out, static_cast<hipStream_t>(stream)));
+}
+
 int sfr_linear_algo_count(void) { return sfr::ALGO_COUNT; }
 
 int sfr_linear_algo_valid(int algo) { return sfr::linear_algo_valid(algo) ? 1 : 0; }

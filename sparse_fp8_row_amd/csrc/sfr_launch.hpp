@@ -18,6 +18,9 @@ hipError_t launch_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols,
 hipError_t launch_compress(const uint8_t* w, int64_t n, int64_t k, uint8_t* values, uint8_t* meta,
                            hipStream_t stream);
 
+// 2:4 pruning of a bf16 matrix (k % 8 == 0); out may be w.
+hipError_t launch_prune_bf16(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t stream);
+
 struct LinearArgs {
   const uint8_t* xq;
   const float* xs;

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "sparse_fp8_rowwise_linear", "sfr_status_string",
+    for n in ("quantize_rowwise_fp8", "compress_2to4_fp8", "prune_2to4_bf16", "sparse_fp8_rowwise_linear",
+              "sfr_status_string",
               "sfr_format_version", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
               "sparse_fp8_scaled_linear", "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_scaled_linear_algo",
               "sparse_fp8_rowwise_linear_dynamic_algo", "sfr_linear_algo_valid",
@@ -164,6 +165,18 @@ def test_dynamic_linear_validation(lib):
 
 
 F8 = 0x100   # SFR_ALGO_ACC_F8
+
+
+def test_prune_validation(lib):
+    p = lib.prune_2to4_bf16
+    assert p(A, 4, 12, A, None) == SHAPE          # k % 8
+    assert p(A, 4, 0, A, None) == SHAPE
+    assert p(A, -1, 8, A, None) == SHAPE
+    assert p(None, 0, 8, None, None) == OK         # no rows
+    assert p(None, 4, 8, A, None) == NULL
+    assert p(A, 4, 8, None, None) == NULL
+    assert p(U, 4, 8, A, None) == ALIGN
+    assert p(A, 4, 8, U, None) == ALIGN
 
 
 def test_linear_algos(lib):

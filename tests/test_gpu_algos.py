@@ -57,8 +57,7 @@ def test_every_algo(gpu, shape):
     case = sfr_inputs.Case(f"algo_{name}", 13, m, n, k, x_fmt=xf, w_fmt=wf, bias=has_bias)
     xb, wb, bb = sfr_inputs.draw_x(case), sfr_inputs.draw_w(case), sfr_inputs.draw_bias(case)
     oxq, oxs = oracle.quantize_rows(xb, xf)
-    owq, ows = oracle.quantize_rows(wb, wf)
-    ov, om = oracle.compress_2to4(owq)
+    ov, om, ows, _ = oracle.prepare_weight(wb, wf)
     ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows, bias=bb)
     hwb = hw_bound(oxq, xf, oxs, oracle.decompress_2to4(ov, om), wf, ows, np.arange(m), np.arange(n))
     xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(xb), FP8_TORCH[xf])

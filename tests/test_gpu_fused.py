@@ -42,8 +42,7 @@ def run_case(gpu, case, wscale="row", seed_shift=0):
     bb = sfr_inputs.draw_bias(case)
     xf, wf = case.x_fmt, case.w_fmt
     oxq, oxs = oracle.quantize_rows(xb, xf)
-    owq, ows = (oracle.quantize_tensor if wscale == "tensor" else oracle.quantize_rows)(wb, wf)
-    ov, om = oracle.compress_2to4(owq)
+    ov, om, ows, _ = oracle.prepare_weight(wb, wf, scaling=wscale)
     ws_full = np.full(case.n, ows[0], np.float32) if wscale == "tensor" else ows
     ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ws_full, bias=bb)
     pw = gpu.prepare_weight(dev_bf16(wb), FP8_TORCH[wf], scaling=wscale)
@@ -112,8 +111,7 @@ def test_dynamic_back_to_back(gpu):
     case_w = sfr_inputs.Case("dyn_seq", 11, 16, n, k, bias=True)
     wb = sfr_inputs.draw_w(case_w)
     pw = gpu.prepare_weight(dev_bf16(wb), torch.float8_e4m3fn)
-    owq, ows = oracle.quantize_rows(wb, E4)
-    ov, om = oracle.compress_2to4(owq)
+    ov, om, ows, _ = oracle.prepare_weight(wb, E4)
     outs, refs = [], []
     for i, m in enumerate((1, 4, 1, 9)):
         case = sfr_inputs.Case("dyn_seq", 20 + i, m, n, k)

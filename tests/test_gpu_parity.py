@@ -85,6 +85,31 @@ def test_compress_bit_exact(gpu, shape, alphabet):
 
 
 # ---------------------------------------------------------------------------
+# prune_2to4_bf16
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 8), (16, 4096), (33, 392), (7, 14336), (6144, 4096)])
+@pytest.mark.parametrize("alphabet", ["normal", "ties"])
+def test_prune_bit_exact(gpu, shape, alphabet):
+    n, k = shape
+    say(f"prune {alphabet} {shape}")
+    rng = np.random.default_rng(n * 3 + k)
+    if alphabet == "normal":
+        w = sfr_inputs.to_bf16_bits(rng.normal(0.0, 0.02, (n, k)))
+        w[rng.random((n, k)) < 0.1] = 0x8000
+    else:
+        w = rng.choice(np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x3C00, 0xBC00, 0x0001, 0x8001, 0x7F7F, 0xFF7F],
+                                np.uint16), (n, k))
+    want = oracle.prune_2to4_bf16(w)
+    t = dev_bf16(w)
+    got = gpu.prune_2to4_bf16(t)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(got), want)
+    gpu.prune_2to4_bf16(t, out=t)          # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(t), want)
+
+
+# ---------------------------------------------------------------------------
 # sparse_fp8_rowwise_linear
 # ---------------------------------------------------------------------------
 def prepare(case):
@@ -106,8 +131,7 @@ def gpu_path(gpu, xb, wb, bb, xf, wf, out_dtype=torch.bfloat16):
 
 def oracle_path(xb, wb, bb, xf, wf, rows=None, cols=None):
     oxq, oxs = oracle.quantize_rows(xb, xf)
-    owq, ows = oracle.quantize_rows(wb, wf)
-    ov, om = oracle.compress_2to4(owq)
+    ov, om, ows, _ = oracle.prepare_weight(wb, wf)
     ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows, bias=bb, rows=rows, cols=cols)
     return oxq, oxs, ov, om, ows, ref
 
@@ -205,8 +229,7 @@ def test_linear_llama_sweep(gpu, shape, seed):
     weights = {}
     for wf in (E4, E5):
         say(f"sweep {shape} weight fmt={wf}")
-        owq, ows = oracle.quantize_rows(wb, wf)
-        ov, om = oracle.compress_2to4(owq)
+        ov, om, ows, _ = oracle.prepare_weight(wb, wf)
         pw = gpu.prepare_weight(dev_bf16(wb), FP8_TORCH[wf])
         torch.cuda.synchronize()
         assert np.array_equal(host_bytes(pw.values), ov) and np.array_equal(host_bytes(pw.meta), om)

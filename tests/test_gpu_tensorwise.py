@@ -91,8 +91,7 @@ def test_scaled_linear(gpu, shape, xk, wk):
         rows = np.unique(np.concatenate([rng.choice(m, 120, replace=False), [0, m - 1]]))
     # oracle: the chosen quantization of each operand, scales broadcast to rows
     oxq, oxs = (oracle.quantize_tensor if xk == "tensor" else oracle.quantize_rows)(xb, xf)
-    owq, ows = (oracle.quantize_tensor if wk == "tensor" else oracle.quantize_rows)(wb, wf)
-    ov, om = oracle.compress_2to4(owq)
+    ov, om, ows, _ = oracle.prepare_weight(wb, wf, scaling=wk)
     xs_full = np.full(m, oxs[0], np.float32) if xk == "tensor" else oxs
     ws_full = np.full(n, ows[0], np.float32) if wk == "tensor" else ows
     ref = oracle.linear(oxq, xf, xs_full, ov, om, wf, ws_full, bias=bb, rows=rows)
