@@ -132,6 +132,26 @@ sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols
  * (at most 4 KB); 0 for sizes it rejects. */
 int64_t sfr_quantize_tensorwise_workspace_bytes(int64_t rows, int64_t cols);
 
+/*
+ * quantize_tensorwise_fp8_noalloc -- quantize_tensorwise_fp8 for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no workspace argument, and the
+ * call allocates nothing.  The workspace is the library's own 4 KB device
+ * array, one copy per GPU, held until the process ends; its address is
+ * looked up on the first call on each device.  Results are bit-identical to
+ * quantize_tensorwise_fp8's.
+ *
+ * Every call on one GPU uses that GPU's array, which keeps the last call's
+ * contents (each call writes every slot it reads before reading it).  Calls
+ * that may overlap on one GPU (different streams, or host threads) race on
+ * the array and must be serialized by the caller.
+ *
+ * Arguments, sizes and errors as quantize_tensorwise_fp8 without the
+ * workspace; a size whose workspace would exceed the array is SFR_ERR_SHAPE
+ * (no accepted size does), and a failed lookup of the array SFR_ERR_LAUNCH.
+ */
+sfr_status quantize_tensorwise_fp8_noalloc(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt,
+                                           uint8_t* q, float* scale, void* stream);
 
 /*
  * compress_2to4_fp8 -- 2:4 semi-structured compression of an FP8 matrix.

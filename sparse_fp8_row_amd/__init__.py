@@ -35,6 +35,7 @@ SFR_SCALE_ROW, SFR_SCALE_TENSOR = 0, 1
 STATUS = {0: "SFR_OK", 1: "SFR_ERR_NULL", 2: "SFR_ERR_SHAPE", 3: "SFR_ERR_ALIGN",
           4: "SFR_ERR_DTYPE", 5: "SFR_ERR_LAUNCH"}
 EXPORTED = ("quantize_rowwise_fp8", "quantize_tensorwise_fp8", "sfr_quantize_tensorwise_workspace_bytes",
+            "quantize_tensorwise_fp8_noalloc",
             "compress_2to4_fp8", "prune_2to4_bf16", "sparse_fp8_rowwise_linear", "sparse_fp8_scaled_linear",
             "sparse_fp8_rowwise_linear_dynamic", "sparse_fp8_rowwise_linear_dynamic_algo",
             "sparse_fp8_scaled_linear_algo", "sfr_linear_algo_count", "sfr_linear_algo_valid",
@@ -65,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.prune_2to4_bf16.argtypes = [P, I64, I64, P, P]
     lib.sparse_fp8_rowwise_linear.argtypes = [P, I, P, I64, I64, P, P, I, P, I64, P, P, I, P]
     lib.quantize_tensorwise_fp8.argtypes = [P, I64, I64, I, P, P, P, I64, P]
+    lib.quantize_tensorwise_fp8_noalloc.argtypes = [P, I64, I64, I, P, P, P]
+    lib.quantize_tensorwise_fp8_noalloc.restype = I
     lib.sparse_fp8_scaled_linear.argtypes = [P, I, P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P]
     lib.sparse_fp8_rowwise_linear_dynamic.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, P]
     lib.sparse_fp8_rowwise_linear_dynamic_algo.argtypes = [P, I, I64, I64, P, P, I, P, I, I64, P, P, I, P, P, I, P]
@@ -149,6 +152,22 @@ def quantize_tensorwise_fp8(x: torch.Tensor, dtype=torch.float8_e4m3fn, stream=N
     _check(lib.quantize_tensorwise_fp8(x.data_ptr(), rows, cols, _fp8_enum(dtype), q.data_ptr(), s.data_ptr(),
                                        work.data_ptr(), nbytes, _stream(stream)), "quantize_tensorwise_fp8")
     return q, s
+
+
+def quantize_tensorwise_fp8_noalloc(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None):
+    """quantize_tensorwise_fp8 into caller-provided q FP8 [rows, cols] and
+    scale float32 [1], on the library's own device workspace (the call
+    allocates nothing).  Calls that overlap on one GPU must be serialized."""
+    for t, nm in ((x, "x"), (q, "q"), (scale, "scale")):
+        _dev(t, nm)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or q.shape != x.shape or scale.shape != (1,) or \
+            scale.dtype != torch.float32:
+        raise ValueError("x bf16 [rows, cols], q FP8 [rows, cols], scale float32 [1]")
+    rows, cols = x.shape
+    _check(load().quantize_tensorwise_fp8_noalloc(x.data_ptr(), rows, cols, _fp8_enum(q.dtype), q.data_ptr(),
+                                                  scale.data_ptr(), _stream(stream)),
+           "quantize_tensorwise_fp8_noalloc")
+    return q, scale
 
 
 def compress_2to4_fp8(wq: torch.Tensor, stream=None):

@@ -51,6 +51,20 @@ sfr_status quantize_tensorwise_fp8(const uint16_t* x, int64_t rows, int64_t cols
       sfr::launch_quantize_tensor(x, rows, cols, dt, q, scale, workspace, static_cast<hipStream_t>(stream)));
 }
 
+sfr_status quantize_tensorwise_fp8_noalloc(const uint16_t* x, int64_t rows, int64_t cols, sfr_fp8_t dt, uint8_t* q,
+                                           float* scale, void* stream) {
+  if (!fp8_ok(dt)) return SFR_ERR_DTYPE;
+  if (rows < 0 || rows > SFR_MAX_DIM || cols <= 0 || cols > SFR_MAX_DIM || cols % 8 != 0 ||
+      rows * cols > kMaxElems)
+    return SFR_ERR_SHAPE;
+  if (rows == 0) return SFR_OK;
+  if (sfr::tensor_workspace_bytes(rows, cols) > sfr::noalloc_workspace_bytes()) return SFR_ERR_SHAPE;
+  if (!x || !q || !scale) return SFR_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return SFR_ERR_ALIGN;
+  return launch_status(
+      sfr::launch_quantize_tensor_noalloc(x, rows, cols, dt, q, scale, static_cast<hipStream_t>(stream)));
+}
+
 sfr_status compress_2to4_fp8(const uint8_t* w, int64_t n, int64_t k, sfr_fp8_t dt, uint8_t* values, uint8_t* meta,
                              void* stream) {
   if (!fp8_ok(dt)) return SFR_ERR_DTYPE;

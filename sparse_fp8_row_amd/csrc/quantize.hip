@@ -18,6 +18,8 @@
 // and the cast sweep, so each input byte is read from HBM once.  Rows longer
 // than 32 chunks per lane (cols > 16384) take a two-sweep path that reads the
 // row again (from L2 in practice).
+#include <atomic>
+
 #include "sfr_device.hpp"
 #include "sfr_launch.hpp"
 #include "sfr_quant.hpp"
@@ -266,6 +268,43 @@ hipError_t launch_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols,
     hipLaunchKernelGGL(tensor_cast_kernel<FMT_E5M2>, dim3(nb), dim3(kTensorThreads), 0, stream, xv, chunks, per, part,
                        nb, reinterpret_cast<uint2*>(q), scale);
   return hipGetLastError();
+}
+
+// Workspace of quantize_tensorwise_fp8_noalloc: one per device, for
+// callers that cannot allocate.  Its largest use is one slot per block of
+// the cast pass (kTensorMaxBlocks 32-bit slots); every slot a call reads is
+// written by that call's first pass, so nothing needs clearing between calls.
+// Host code must use the address hipGetSymbolAddress returns for the current
+// device, never the array's name.
+static __device__ __align__(256) uint32_t scratch[kTensorMaxBlocks];
+
+int64_t noalloc_workspace_bytes() { return (int64_t)sizeof(scratch); }
+
+// The current device's copy of `scratch` (looked up once per device).
+static hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cache[dev].store(p, std::memory_order_release);  // every thread stores the same address
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_tensor_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                          float* scale, hipStream_t stream) {
+  if (tensor_workspace_bytes(rows, cols) > noalloc_workspace_bytes()) return hipErrorInvalidValue;
+  void* work = nullptr;
+  hipError_t e = scratch_address(&work);
+  if (e != hipSuccess) return e;
+  return launch_quantize_tensor(x, rows, cols, fmt, q, scale, work, stream);
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,

@@ -14,6 +14,10 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fm
 int64_t tensor_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* scale,
                                   void* workspace, hipStream_t stream);
+// The same on the library's own per-device workspace of noalloc_workspace_bytes().
+int64_t noalloc_workspace_bytes();
+hipError_t launch_quantize_tensor_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                          float* scale, hipStream_t stream);
 
 hipError_t launch_compress(const uint8_t* w, int64_t n, int64_t k, uint8_t* values, uint8_t* meta,
                            hipStream_t stream);
