@@ -1287,13 +1287,31 @@ __global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      if constexpr (ACC == ACC_F32) {
+        // the activation half widened once for the RT row tiles
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const uint8_t* rt = region + t * kUnitLds;
-        const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
-        const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
-        if (s & 1) acc1[t] = mma_step<XF, WF, ACC>(a, b[s], acc1[t], idx);
-        else acc0[t] = mma_step<XF, WF, ACC>(a, b[s], acc0[t], idx);
+        for (int hh = 0; hh < 2; ++hh) {
+          const v8i bw = hh ? widen_b_half<XF, 1>(b[s]) : widen_b_half<XF, 0>(b[s]);
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const uint8_t* rt = region + t * kUnitLds;
+            const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
+            const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
+            const v4i aw = hh ? widen_a_half<WF, 1>(a) : widen_a_half<WF, 0>(a);
+            const int ix = hh ? idx_half<1>(idx) : idx_half<0>(idx);
+            if (s & 1) acc1[t] = smfmac16_bf16(aw, bw, acc1[t], ix);
+            else acc0[t] = smfmac16_bf16(aw, bw, acc0[t], ix);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const uint8_t* rt = region + t * kUnitLds;
+          const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
+          const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
+          if (s & 1) acc1[t] = smfmac16<XF, WF>(a, b[s], acc1[t], idx);
+          else acc0[t] = smfmac16<XF, WF>(a, b[s], acc0[t], idx);
+        }
       }
     }
     // the region's reads are complete (their values fed the MFMAs) before
