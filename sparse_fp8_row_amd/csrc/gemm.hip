@@ -679,11 +679,15 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
       const uint8_t* base = smem + (kt % S) * C::STAGE;
       const int mo = 16 * ((kt % MB) ^ (r16 & 7)) + ((kt / MB) & 1) * C::META_BLOCK - (int)(base - smem);
       if constexpr (ACC == ACC_F32) {
-        // the step as two half steps (see smfmac16_bf16): per half, the
-        // weight fragments' half widened once, then each activation block's
-        // half (two 8-byte LDS reads) widened once and fed to FN
-        // instructions.  Holding one half at a time keeps registers free for
-        // the LDS reads to run ahead of the matrix instructions.
+        // The step as 2 FM (activation block, half) pairs, in that order (see
+        // smfmac16_bf16).  Both halves of the weight fragments are widened
+        // at the start; each activation block is read whole (two 16-byte LDS
+        // reads, PD blocks ahead) and the operand of pair q + 1 is widened
+        // while the FN instructions of pair q run: the scheduling groups
+        // below put two of those conversions after each instruction (seven
+        // in pair 0, which also widens the second weight half), so the
+        // conversions issue while the matrix core is busy instead of
+        // between its instruction groups.
         v4i a[C::FN];
         int idx[C::FN];
 #pragma unroll
@@ -691,39 +695,47 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
           a[fn] = *reinterpret_cast<const v4i*>(base + a_off[fn]);
           idx[fn] = *reinterpret_cast<const int*>(base + i_off[fn] + mo);
         }
-        // the 2 FM (half, activation block) pairs in order, the activation
-        // halves read PD pairs ahead of their instructions
-        constexpr int NQ = 2 * C::FM, PD = 3;
-        uint2 rlo[NQ], rhi[NQ];
-        auto read_q = [&](int q) __attribute__((always_inline)) {
-          const int h = q / C::FM, fm = q % C::FM;
-          rlo[q] = *reinterpret_cast<const uint2*>(base + b_off0[fm] + 8 * h);
-          rhi[q] = *reinterpret_cast<const uint2*>(base + b_off1[fm] + 8 * h);
+        constexpr int PD = 2;
+        auto read_b = [&](int fm) __attribute__((always_inline)) {
+          const v4i lo = *reinterpret_cast<const v4i*>(base + b_off0[fm]);
+          const v4i hi = *reinterpret_cast<const v4i*>(base + b_off1[fm]);
+          return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
+        v8i braw[C::FM];
 #pragma unroll
-        for (int q = 0; q < PD; ++q) read_q(q);
-        v4i aw[C::FN];
-        int ix[C::FN];
+        for (int f = 0; f < PD; ++f) braw[f] = read_b(f);
+        v4i aw[2][C::FN];
+        int ix[2][C::FN];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int h = q / C::FM, fm = q % C::FM;
-          if (q + PD < NQ) read_q(q + PD);
-          if (fm == 0) {
+        for (int fn = 0; fn < C::FN; ++fn) {
+          aw[0][fn] = widen_a_half<WF, 0>(a[fn]);
+          ix[0][fn] = idx_half<0>(idx[fn]);
+        }
+        v8i bw[2];
+        bw[0] = widen_b_half<XF, 0>(braw[0]);
+#pragma unroll
+        for (int q = 0; q < 2 * C::FM; ++q) {
+          const int fm = q >> 1, h = q & 1;
+          const bool rd = h == 0 && fm + PD < C::FM;
+          if (rd) braw[fm + PD] = read_b(fm + PD);
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[h][fn], bw[h], acc[fn][fm], ix[h][fn]);
+          if (q == 0) {
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn) {
-              aw[fn] = h ? widen_a_half<WF, 1>(a[fn]) : widen_a_half<WF, 0>(a[fn]);
-              ix[fn] = h ? idx_half<1>(idx[fn]) : idx_half<0>(idx[fn]);
+              aw[1][fn] = widen_a_half<WF, 1>(a[fn]);
+              ix[1][fn] = idx_half<1>(idx[fn]);
             }
           }
-          // widen_b_half<XF, h> of the activation fragment whose half h these are
-          const v8i bw = v8i{widen2<XF, false>((int)rlo[q].x), widen2<XF, true>((int)rlo[q].x),
-                             widen2<XF, false>((int)rlo[q].y), widen2<XF, true>((int)rlo[q].y),
-                             widen2<XF, false>((int)rhi[q].x), widen2<XF, true>((int)rhi[q].x),
-                             widen2<XF, false>((int)rhi[q].y), widen2<XF, true>((int)rhi[q].y)};
-          __builtin_amdgcn_s_setprio(1);
+          if (q + 1 < 2 * C::FM) bw[h ^ 1] = h ? widen_b_half<XF, 0>(braw[fm + 1]) : widen_b_half<XF, 1>(braw[fm]);
+          // scheduling groups (0x100 LDS read, 0x008 matrix, 0x002 other ALU)
+          if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[fn], bw, acc[fn][fm], ix[fn]);
-          __builtin_amdgcn_s_setprio(0);
+          for (int fn = 0; fn < C::FN; ++fn) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q == 0) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
         }
         continue;
       }
@@ -1196,11 +1208,15 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 // chunk ^ (row & 7) (a permutation inside 128-byte groups, applied to the
 // source addresses of each 1 KB load), which makes the MFMA-layout LDS reads
 // conflict-free.  RT = 2 halves the activation traffic (every workgroup reads
-// all of the activation) at half the workgroups.
+// all of the activation) at half the workgroups.  Its 20 KB of LDS per
+// wavefront allow at most two workgroups per CU with four or more wavefronts,
+// so its register budget is that of two (256 per lane): the 64 registers of
+// activation operands and the widened operands of the binary32-grade step
+// then fit without spilling.
 constexpr int kUnitK = 1024;
 constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
 template <int XF, int WF, int OUT, int ACC, int RT, bool X1>
-__global__ __launch_bounds__(512, 4) void linear_decode_unit_kernel(
+__global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int xs_stride, int ws_stride) {
