@@ -7,7 +7,7 @@
 // row/column scales and the bias are applied in the epilogue of the same
 // kernel, and the result leaves as bf16.
 //
-// Instruction: V_SMFMAC_F32_16X16X128_{FP8,BF8}_{FP8,BF8}.  The sparse A
+// Instructions: V_SMFMAC_F32_16X16X128_{FP8,BF8}_{FP8,BF8}.  The sparse A
 // operand is the compressed weight (16 output rows, 128 dense k per
 // instruction, 64 kept bytes per row plus 2-bit positions), the dense B
 // operand is the activation transposed (16 tokens x 128 k), so one
@@ -17,27 +17,42 @@
 // untouched.  Each lane of a D block holds four consecutive n of one m, which
 // is what a row-major [M, N] output wants: 8-byte bf16 stores.
 //
-// Two kernels:
-//  * tiled:  a workgroup computes a BN x BM tile of out^T.  Per 128-wide k step
-//    it stages BN rows of compressed weight (64 B values + 16 B metadata per
-//    row) and BM rows of activation (128 B per row) in LDS with
-//    global_load_lds (memory -> LDS without passing through registers), in S
-//    buffers: the loads of step k+S-1 are in flight while the MFMAs of step k
-//    run.  LDS rows are XOR-swizzled in 16-byte chunks so that the 8 lanes the
-//    LDS serves together read 8 different 16-byte bank groups.  Tiles are
-//    assigned so that each XCD (workgroup id mod 8) works on one contiguous
-//    run of tiles, walked in groups of G n-tiles, which keeps the weight and
-//    activation panels that neighbouring workgroups share in that XCD's L2.
-//    The prefill shape runs 256 x 256 tiles on 8 wavefronts (64 x 128 each,
-//    two per SIMD) with S = 2; each wavefront reads its activation blocks
-//    first and then streams its weight blocks one ahead of their MFMAs.
-//  * decode: for M <= 16, where the weight read is everything.  A workgroup
-//    owns 16 weight rows; its wavefronts split the k steps between them,
-//    stream the compressed weight straight from HBM into registers (no LDS
-//    staging: every byte is used by exactly one instruction), and reduce
-//    their partial 16x16 sums through LDS in a fixed order (deterministic).
-//    Tokens beyond M are zero columns of B, the padding-to-16 idea of
-//    pytorch/ao PR #1734 ("promote blocksparse from prototype ...").
+// Accumulation (template parameter ACC).  The FP8 instruction adds the
+// products of one instruction in fixed point 13 bits below the largest of
+// them, which is outside the layer's binary32 accuracy on cancelling inputs,
+// so by default (ACC_F32) each 128-k step runs as two
+// V_SMFMAC_F32_16X16X64_BF16 instructions on operands widened exactly to
+// bf16 (sfr_device.hpp, mma_step); ACC_F8 (algorithm ids with the FP8
+// accumulation flag) runs the FP8 instruction.  Same layouts, same loads.
+//
+// Kernels:
+//  * tiled (linear_tiled_kernel): a workgroup computes a BN x BM tile of
+//    out^T.  Per 128-wide k step it stages BN rows of compressed weight (64 B
+//    values, metadata in blocks of steps) and BM rows of activation (128 B per
+//    row) in LDS with global->LDS loads, in S buffers: the loads of step k+S-1
+//    are in flight while the MFMAs of step k run.  LDS rows are XOR-swizzled
+//    in 16-byte chunks so that the lanes the LDS serves together read
+//    different banks.  Tiles are assigned so that each XCD (workgroup id
+//    mod 8) works on one contiguous run of tiles, walked in groups of G
+//    n-tiles, which keeps the weight and activation panels that neighbouring
+//    workgroups share in that XCD's L2.
+//  * persistent (linear_persistent_kernel): the prefill configuration, one
+//    workgroup per CU walking 256 x 256 tiles; 8 wavefronts (64 x 128 each,
+//    two per SIMD), wavefronts 0-3 also issue the global->LDS loads of the
+//    next stage and 4-7 store the previous tile's output.
+//  * wide (linear_wide_kernel, ACC_F8 only): 256 x 256 tiles on 4 wavefronts
+//    (128 x 128 each, accumulators in the accumulation registers).
+//  * decode (linear_decode_unit_kernel): for M <= 64, where the weight read is
+//    everything.  A workgroup owns 16 or 32 weight rows; its wavefronts split
+//    the k range in units of 1024, each putting its unit's weight block into
+//    its own LDS region (global->LDS, whole cache lines) and its activation
+//    into registers, then reduce their partial 16x16 sums through LDS in a
+//    fixed order (deterministic).  Tokens beyond M are padding columns of B
+//    whose outputs are never stored, the padding-to-16 idea of pytorch/ao PR
+//    #1734 ("promote blocksparse from prototype ...").
+//    linear_decode_kernel streams the weight into registers instead (any K
+//    that is a multiple of 128), and linear_decode_unit_fused1_kernel also
+//    quantizes a single bf16 activation row itself.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -1215,7 +1230,8 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 // then fit without spilling.
 constexpr int kUnitK = 1024;
 constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
-template <int XF, int WF, int OUT, int ACC, int RT, bool X1>
+enum { XM_DIRECT = 0, XM_ONE_ROW = 1, XM_PERMUTED = 2 };
+template <int XF, int WF, int OUT, int ACC, int RT, int XM>
 __global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
@@ -1239,9 +1255,21 @@ __global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kerne
   // workgroup row blockIdx.y takes activation rows mb .. mb + 15 (M up to
   // 64: the weight block is read once per 16 rows, mostly from L2).  Rows
   // past the last, Mc, read row Mc - 1: MFMA output column m depends on
-  // activation row m alone, and those columns are never stored
+  // activation row m alone, and those columns are never stored.
+  // Activation loads (XM): XM_ONE_ROW, M == 1: one 16-byte chunk per lane,
+  // broadcast per step (below).  XM_DIRECT: in the MFMA layout (lane (m, g):
+  // row m, chunk g), sixteen rows under sixteen neighbouring lanes, which the
+  // vector memory unit serves as one cache access per lane.  XM_PERMUTED:
+  // row-contiguously (lane L: row L / 4, chunk L % 4 of each 64-byte half
+  // step, four neighbouring lanes on one 64-byte run), then moved into the
+  // MFMA layout by a lane permutation (ds_bpermute, eight per step); it pays
+  // for itself when most of the 16 rows are distinct (measured: M = 16
+  // faster by up to 1.9 us, M = 4 slower by 0.4-0.8 us than XM_DIRECT).
   const int mb = blockIdx.y * 16, Mc = min(M - mb, 16);
-  const uint8_t* xrow = xq + (int64_t)(mb + min(r16, Mc - 1)) * K + 16 * lg;
+  const uint8_t* xrow =
+      XM == XM_PERMUTED ? xq + (int64_t)(mb + min(lane >> 2, Mc - 1)) * K + 16 * (lane & 3)
+                        : xq + (int64_t)(mb + min(r16, Mc - 1)) * K + 16 * lg;
+  const int xsrc = 4 * (4 * r16 + lg);  // byte address of the source lane of (r16, lg)
   // LDS read offsets: step s's values chunk 4s + lg of row r16 sits at chunk
   // (4s + lg) ^ (r16 & 7) = 8 (s >> 1) + ab[s & 1]; its metadata chunk at s ^ (r16 & 7)
   const int r7 = r16 & 7;
@@ -1282,7 +1310,7 @@ __global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kerne
     }
     v8i b[8];
     v4i x1;
-    if constexpr (X1) {
+    if constexpr (XM == XM_ONE_ROW) {
       // one activation row: lane (r16, lg) holds chunk 8 (r16 >> 1) + 4 (r16 & 1) + lg
       // of the unit, i.e. the half r16 & 1 of step r16 >> 1 that lane group lg needs
       x1 = *reinterpret_cast<const v4i*>(xq + u0 * kUnitK + 128 * (r16 >> 1) + 64 * (r16 & 1) + 16 * lg);
@@ -1296,13 +1324,17 @@ __global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kerne
       }
     }
     wait_vmcnt<0>();
-    if constexpr (X1) {
+    if constexpr (XM == XM_ONE_ROW) {
       // step s's operand: lanes 2s and 2s + 1 of each 16-lane row, broadcast
       // to the whole row (DPP row_newbcast)
       row_bcast_steps(b, x1, std::make_integer_sequence<int, 8>{});
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      if constexpr (XM == XM_PERMUTED) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) b[s][d] = __builtin_amdgcn_ds_bpermute(xsrc, b[s][d]);
+      }
       if constexpr (ACC == ACC_F32) {
         // the activation half widened once for the RT row tiles
 #pragma unroll
@@ -1433,9 +1465,9 @@ inline int unit_waves(int64_t k) {
   return (nu + per - 1) / per;
 }
 
-template <int XF, int WF, int OUT, int ACC, int RT, bool X1>
+template <int XF, int WF, int OUT, int ACC, int RT, int XM>
 hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
-  auto kern = linear_decode_unit_kernel<XF, WF, OUT, ACC, RT, X1>;
+  auto kern = linear_decode_unit_kernel<XF, WF, OUT, ACC, RT, XM>;
   const int nw = unit_waves(a.k);
   const unsigned lds = (unsigned)(nw * RT * kUnitLds);
   static bool attr_set = false;  // benign race: every thread sets the same value
@@ -1453,8 +1485,13 @@ hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
 
 template <int XF, int WF, int OUT, int ACC, int RT>
 hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
-  if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, true>(a, stream);
-  return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, false>(a, stream);
+  // the permuted activation loads above 8 rows on the shapes whose weight
+  // stream is long enough to hide the permutation (measured on the Llama
+  // shapes at M = 16: 0.3-1.9 us faster at N >= 6144 or K >= 8192, 0.15 us
+  // slower at N = K = 4096)
+  if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_ONE_ROW>(a, stream);
+  if (a.m <= 8 || (a.n < 6144 && a.k < 8192)) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_DIRECT>(a, stream);
+  return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_PERMUTED>(a, stream);
 }
 
 // ---------------------------------------------------------------------------
