@@ -698,10 +698,10 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
         // smfmac16_bf16).  Both halves of the weight fragments are widened
         // at the start; each activation block is read whole (two 16-byte LDS
         // reads, PD blocks ahead) and the operand of pair q + 1 is widened
-        // while the FN instructions of pair q run: the scheduling groups
-        // below put two of those conversions after each instruction (seven
-        // in pair 0, which also widens the second weight half), so the
-        // conversions issue while the matrix core is busy instead of
+        // while the FN instructions of pair q run: 8 / FN of those
+        // conversions follow each instruction (and in pair 0 also one
+        // fragment's second weight half), held in place by scheduling
+        // barriers, so they issue while the matrix core is busy instead of
         // between its instruction groups.
         v4i a[C::FN];
         int idx[C::FN];
@@ -728,28 +728,33 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
         }
         v8i bw[2];
         bw[0] = widen_b_half<XF, 0>(braw[0]);
+        constexpr int EPF = 8 / C::FN;  // conversions after each instruction
+        static_assert(8 % C::FN == 0, "conversions spread evenly over the instructions");
 #pragma unroll
         for (int q = 0; q < 2 * C::FM; ++q) {
           const int fm = q >> 1, h = q & 1;
-          const bool rd = h == 0 && fm + PD < C::FM;
-          if (rd) braw[fm + PD] = read_b(fm + PD);
+          if (h == 0 && fm + PD < C::FM) braw[fm + PD] = read_b(fm + PD);
+          // pair q + 1 uses half nh of block nfm; its element e (widen_b_half)
+          // is half (e & 1) of FP8 word 2 nh + ((e >> 1) & 1) + 4 (e >> 2)
+          const bool more = q + 1 < 2 * C::FM;
+          const int nfm = fm + h, nh = h ^ 1;
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) acc[fn][fm] = smfmac16_bf16(aw[h][fn], bw[h], acc[fn][fm], ix[h][fn]);
-          if (q == 0) {
+          for (int fn = 0; fn < C::FN; ++fn) {
+            acc[fn][fm] = smfmac16_bf16(aw[h][fn], bw[h], acc[fn][fm], ix[h][fn]);
+            if (more) {
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
+              for (int e = fn * EPF; e < (fn + 1) * EPF; ++e) {
+                const int w = braw[nfm][2 * nh + ((e >> 1) & 1) + 4 * (e >> 2)];
+                bw[nh][e] = (e & 1) ? widen2<XF, true>(w) : widen2<XF, false>(w);
+              }
+            }
+            if (q == 0) {
               aw[1][fn] = widen_a_half<WF, 1>(a[fn]);
               ix[1][fn] = idx_half<1>(idx[fn]);
             }
-          }
-          if (q + 1 < 2 * C::FM) bw[h ^ 1] = h ? widen_b_half<XF, 0>(braw[fm + 1]) : widen_b_half<XF, 1>(braw[fm]);
-          // scheduling groups (0x100 LDS read, 0x008 matrix, 0x002 other ALU)
-          if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q == 0) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-            else __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            // program order is issue order: each instruction is followed by
+            // the conversions that can run while it occupies the matrix core
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         continue;

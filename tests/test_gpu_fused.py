@@ -1,12 +1,14 @@
 """GPU parity of sparse_fp8_rowwise_linear_dynamic (activation quantization
-fused into the decode GEMM launch for one activation row).
+fused into the decode GEMM launch for one activation row; two launches,
+quantization then the linear layer, for other shapes).
 
 The codes and scales it writes are compared bit for bit with the oracle's
 row-wise quantization, the output with the oracle's linear layer (same rules
 as the row-wise tests), on every fused shape class (K from one 1024-k unit
 to 16384, one and two units per wavefront, uneven unit counts, grids smaller
 and larger than the chip holds at once, row and tensor weight scales, an
-all-zero row) and on shapes that take the two-launch path.
+all-zero row) and on the two-launch path (row counts 2 .. 17 including odd
+ones, K not a multiple of 1024 or above 16384, all-zero rows).
 """
 import sys
 
@@ -96,9 +98,35 @@ def test_dynamic_fused_zero_row(gpu):
     assert np.array_equal(host_bf16_bits(y)[0], bb)
 
 
-# shapes that take the two-launch path: m > 1, k not a multiple of 1024, k > 16384
-@pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 4096, 14336), (16, 4096, 4096),
-                                   (2, 1024, 1024), (4, 4096, 4096), (1, 4096, 640), (1, 256, 17408)],
+def test_dynamic_zero_rows_multi(gpu):
+    # several rows with all-zero rows (both zero signs) among them
+    n, k = 4096, 3072
+    case = sfr_inputs.Case("dyn_zero_m", 14, 6, n, k, bias=True)
+    xb = sfr_inputs.draw_x(case)
+    xb[2] = 0
+    xb[2, 1::3] = 0x8000
+    xb[5] = 0x8000
+    wb = sfr_inputs.draw_w(case)
+    bb = sfr_inputs.draw_bias(case)
+    pw = gpu.prepare_weight(dev_bf16(wb), torch.float8_e4m3fn)
+    y, xq, xs = gpu.sparse_fp8_rowwise_linear_dynamic(dev_bf16(xb), pw.values, pw.meta, pw.scale, dev_bf16(bb))
+    torch.cuda.synchronize()
+    oxq, oxs = oracle.quantize_rows(xb, E4)
+    assert np.array_equal(host_bytes(xq), oxq)
+    assert np.array_equal(host_f32(xs).view(np.uint32), oxs.view(np.uint32))
+    ov, om, ows, _ = oracle.prepare_weight(wb, E4)
+    r = check_bf16(host_bf16_bits(y), oracle.linear(oxq, E4, oxs, ov, om, E4, ows, bias=bb))
+    say(f"  zero rows {r}")
+    assert r["bad"] == 0, r
+    assert np.array_equal(host_bf16_bits(y)[2], bb) and np.array_equal(host_bf16_bits(y)[5], bb)
+
+
+# shapes that take the two-launch path: m > 1 (16 or 32 weight rows per
+# workgroup in the linear layer), k not a multiple of 1024, k > 16384
+@pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 6144, 16384), (1, 4096, 640),
+                                   (1, 256, 17408), (3, 1024, 640), (2, 4096, 4096), (4, 4096, 4096),
+                                   (16, 4096, 4096), (3, 1024, 2048), (7, 4096, 14336), (16, 4096, 14336),
+                                   (16, 14336, 4096), (8, 6144, 4096), (13, 6144, 9216), (5, 2080, 1024)],
                          ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
 def test_dynamic_two_launch(gpu, shape):
     m, n, k = shape

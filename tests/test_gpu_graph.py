@@ -72,6 +72,20 @@ def test_graph_fused_one_row(gpu):
     replay_matches(step, eager)
 
 
+def test_graph_dynamic_rows(gpu):
+    case = sfr_inputs.Case("graph", 43, 16, 14336, 4096, bias=True)
+    x = dev_bf16(sfr_inputs.draw_x(case))
+    pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)))
+    b = dev_bf16(sfr_inputs.draw_bias(case))
+
+    def step():
+        return gpu.sparse_fp8_rowwise_linear_dynamic(x, pw.values, pw.meta, pw.scale, b)
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    replay_matches(step, eager)
+
+
 def test_graph_bsr(gpu):
     case = sfr_inputs.Case("graph", 42, 4, 4096, 4096, bias=True)
     x = dev_bf16(sfr_inputs.draw_x(case))
