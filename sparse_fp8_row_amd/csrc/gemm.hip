@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_tiled_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave / WM, wm = wave % WM;
   const int r16 = lane & 15, lg = lane >> 4;
-  const int64_t ldv = K / 2, ldm = K / 8, ldx = K;
+  const int64_t ldm = K / 8;
 
   // ---- this wavefront's share of the per-stage loads (global -> LDS) ----
   const StageLoader<BN, BM, C::NW, MB == 0> loader(values, meta, xq, K, N, M, n0, m0, wave, lane);
