@@ -452,7 +452,7 @@ def bench_algo_search():
 # Decode-shaped workloads: the 4096 x 4096 o-projection as the decode
 # configuration (M in {1, 4, 16}, bf16 bias; batched decode M in {32, 64}),
 # and the qkv, up and down projections of the layer sweep (seed 0, no bias).
-DECODE_SHAPES = (("o", (1, 4, 16, 32, 64)), ("qkv", (1, 4, 16)), ("up", (1, 4, 16)), ("down", (1, 4, 16)))
+DECODE_SHAPES = (("o", (1, 2, 4, 16, 32, 64)), ("qkv", (1, 2, 4, 16)), ("up", (1, 2, 4, 16)), ("down", (1, 2, 4, 16)))
 
 
 def decode_case(sfr_inputs, shape, m):

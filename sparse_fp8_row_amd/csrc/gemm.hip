@@ -1519,6 +1519,7 @@ hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
 // writes the codes and the scale to xq / xs.  A wavefront holds at most 2
 // units of the activation (K <= 16384 with 8 wavefronts).
 constexpr int kFusedMaxUnitsPerWave = 2;
+constexpr int kCodeRow = kUnitK + 16;  // LDS stride of a row's codes (several rows)
 
 // First loads of the fused decode kernel: the wavefront's activation chunks
 // (global -> LDS into xl), then its first unit's weight block (into wl), a
@@ -1526,18 +1527,21 @@ constexpr int kFusedMaxUnitsPerWave = 2;
 // read back.  xl and wl are restrict parameters of an inlined function, so
 // the compiler can tell the activation reads from the pending weight loads
 // and does not make them wait for the whole stream.
-template <int UPW>
+template <int UPW, int MR>
 __device__ __forceinline__ void fused_first_loads(uint8_t* __restrict__ xl, uint8_t* __restrict__ wl,
                                                   const uint16_t* __restrict__ x, const uint8_t* vu, const uint8_t* mu,
-                                                  const uint32_t (&voff)[4], uint32_t moff, int K, int NU, int wave,
-                                                  int NW, int xoff, int lane, uint4 (&xa)[UPW][2]) {
+                                                  const uint32_t (&voff)[4], uint32_t moff, int M, int K, int NU,
+                                                  int wave, int NW, int xoff, int lane, uint4 (&xa)[UPW][MR][2]) {
 #pragma unroll
   for (int c = 0; c < UPW; ++c) {
     const int u0 = min(wave + c * NW, NU - 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      __builtin_amdgcn_global_load_lds((void*)(x + (int64_t)u0 * kUnitK + xoff + 8 * h), (void*)(xl + (2 * c + h) * 1024),
-                                       16, 0, 0);
+    for (int r = 0; r < MR; ++r) {
+      const uint16_t* xr = x + (int64_t)min(r, M - 1) * K + (int64_t)u0 * kUnitK + xoff;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_global_load_lds((void*)(xr + 8 * h), (void*)(xl + ((c * MR + r) * 2 + h) * 1024), 16, 0, 0);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -1549,27 +1553,54 @@ __device__ __forceinline__ void fused_first_loads(uint8_t* __restrict__ xl, uint
 #pragma unroll
   for (int c = 0; c < UPW; ++c)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) xa[c][h] = reinterpret_cast<const uint4*>(xl + (2 * c + h) * 1024)[lane];
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xa[c][r][h] = reinterpret_cast<const uint4*>(xl + ((c * MR + r) * 2 + h) * 1024)[lane];
 }
 
-template <int XF, int WF, int OUT, int ACC, int NWMAX>
+// Step S of a unit for several activation rows: lane (m, g) reads its row's
+// operand (the codes 128 S + 16 g and 128 S + 64 + 16 g of the unit, as
+// row_bcast_pair would broadcast them) from the codes the wavefront stored in
+// LDS; cb points at the lane's row of the unit, offset by 16 g.
+template <int XF, int WF, int ACC, int S>
+__device__ __forceinline__ void xl_step(v4f& acc0, v4f& acc1, const uint8_t* cb, const uint8_t* region,
+                                        uint32_t a_even, uint32_t a_odd, uint32_t i_row, int r7) {
+  const v4i a = *reinterpret_cast<const v4i*>(region + ((S & 1) ? a_odd : a_even) + 128 * (S >> 1));
+  const int idx = *reinterpret_cast<const int*>(region + i_row + 16 * (S ^ r7));
+  const v4i lo = *reinterpret_cast<const v4i*>(cb + 128 * S);
+  const v4i hi = *reinterpret_cast<const v4i*>(cb + 128 * S + 64);
+  const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  if constexpr (S & 1) acc1 = mma_step<XF, WF, ACC>(a, b, acc1, idx);
+  else acc0 = mma_step<XF, WF, ACC>(a, b, acc0, idx);
+}
+template <int XF, int WF, int ACC, int... S>
+__device__ __forceinline__ void xl_unit(v4f& acc0, v4f& acc1, const uint8_t* cb, const uint8_t* region,
+                                        uint32_t a_even, uint32_t a_odd, uint32_t i_row, int r7,
+                                        std::integer_sequence<int, S...>) {
+  (xl_step<XF, WF, ACC, S>(acc0, acc1, cb, region, a_even, a_odd, i_row, r7), ...);
+}
+
+template <int XF, int WF, int OUT, int ACC, int NWMAX, int MR>
 __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_unit_fused1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
     const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const float* __restrict__ ws,
-    const uint16_t* __restrict__ bias, void* __restrict__ out, int N, int K, int ws_stride) {
+    const uint16_t* __restrict__ bias, void* __restrict__ out, int M, int N, int K, int ws_stride) {
   // dynamic LDS: the weight regions, then the activation chunks, then the
   // wavefront maxima
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  // a wavefront holds 2 units with 8 wavefronts (K up to 16384; 1 or 2 rows)
+  static_assert(MR < 4 || NWMAX <= 4, "3 or 4 rows: K up to 4096");
   constexpr int UPW0 = NWMAX == 8 ? kFusedMaxUnitsPerWave : 1;
+  static_assert((UPW0 * MR - 1) * kCodeRow + kUnitK <= UPW0 * MR * 2048, "codes fit the staging area");
   uint8_t* xbase = smem + NWMAX * kUnitLds;
-  uint32_t* wmax = reinterpret_cast<uint32_t*>(xbase + NWMAX * UPW0 * 2048);
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(xbase + NWMAX * UPW0 * MR * 2048);  // [NW][MR]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NW = blockDim.x / 64;
   const int r16 = lane & 15, lg = lane >> 4;
   const int NU = K / kUnitK;
   // this wavefront's units: 1, or 2 when there are more units than 8 wavefronts
-  constexpr int UPW = NWMAX == 8 ? kFusedMaxUnitsPerWave : 1;
+  constexpr int UPW = UPW0;
   const int nuw = (NU - wave + NW - 1) / NW;
   uint8_t* region = smem + wave * kUnitLds;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
@@ -1611,37 +1642,70 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
   // 16 l of each 1 KB), issued before the weight loads: all pending loads are
   // then of one kind and complete in issue order, so once at most the weight
   // loads are pending (vmcnt(10)) the activation has landed
-  uint4 xa[UPW][2];
-  fused_first_loads<UPW>(xbase + wave * UPW0 * 2048, region, x, values + n0 * (K / 2) + wave * (kUnitK / 2),
-                         meta + n0 * (K / 8) + wave * (kUnitK / 8), voff, moff, K, NU, wave, NW, xoff, lane, xa);
+  uint4 xa[UPW][MR][2];
+  uint8_t* xw = xbase + wave * UPW0 * MR * 2048;
+  fused_first_loads<UPW, MR>(xw, region, x, values + n0 * (K / 2) + wave * (kUnitK / 2),
+                             meta + n0 * (K / 8) + wave * (kUnitK / 8), voff, moff, M, K, NU, wave, NW, xoff, lane,
+                             xa);
 
-  // 2. row maximum over lanes, then wavefronts
-  uint32_t mx = 0;
+  // 2. each row's maximum over lanes, then wavefronts
+  uint32_t mx[MR];
 #pragma unroll
-  for (int c = 0; c < UPW; ++c)
-    if (c < nuw) mx = mag_max8(xa[c][1], mag_max8(xa[c][0], mx));
-  mx = wave_max(mx);
-  if (lane == 0) wmax[wave] = mx;
+  for (int r = 0; r < MR; ++r) {
+    mx[r] = 0;
+#pragma unroll
+    for (int c = 0; c < UPW; ++c)
+      if (c < nuw) mx[r] = mag_max8(xa[c][r][1], mag_max8(xa[c][r][0], mx[r]));
+    mx[r] = wave_max(mx[r]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r) wmax[wave * MR + r] = mx[r];
+  }
   lds_barrier();
-  uint32_t mm = wmax[0];
-  for (int w = 1; w < NW; ++w) mm = max(mm, wmax[w]);
-  const float sc = bf16_to_f32(mm) / Fp8<XF>::fmax;
-  const float rc = 1.0f / sc;
+  float sc[MR], rc[MR];
+  bool zr[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    uint32_t mm = wmax[r];
+    for (int w = 1; w < NW; ++w) mm = max(mm, wmax[w * MR + r]);
+    zr[r] = mm == 0;
+    sc[r] = bf16_to_f32(mm) / Fp8<XF>::fmax;
+    rc[r] = 1.0f / sc[r];
+  }
 
   // 3. codes of this wavefront's units (workgroup 0 also stores them)
-  v4i x1[UPW];
+  v4i x1[UPW][MR];
   const bool out0 = blockIdx.x == 0;
 #pragma unroll
   for (int c = 0; c < UPW; ++c) {
     if (c < nuw) {
-      const uint2 lo = mm == 0 ? zero8(xa[c][0]) : cast8<XF>(xa[c][0], sc, rc);
-      const uint2 hi = mm == 0 ? zero8(xa[c][1]) : cast8<XF>(xa[c][1], sc, rc);
-      x1[c] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      if (out0) *reinterpret_cast<v4i*>(xq + (int64_t)(wave + c * NW) * kUnitK + xoff) = x1[c];
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const uint2 lo = zr[r] ? zero8(xa[c][r][0]) : cast8<XF>(xa[c][r][0], sc[r], rc[r]);
+        const uint2 hi = zr[r] ? zero8(xa[c][r][1]) : cast8<XF>(xa[c][r][1], sc[r], rc[r]);
+        x1[c][r] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+        if (out0 && r < M) *reinterpret_cast<v4i*>(xq + (int64_t)r * K + (wave + c * NW) * kUnitK + xoff) = x1[c][r];
+        // several rows: the codes go to this wavefront's staging area (its
+        // bf16 chunks are already in registers), in k order per row and unit,
+        // rows 1040 bytes apart so that the rows' operand reads of a step
+        // fall in different LDS banks
+        if constexpr (MR > 1) *reinterpret_cast<v4i*>(xw + (c * MR + r) * kCodeRow + xoff) = x1[c][r];
+      }
     }
   }
-  const float xsm = mm == 0 ? 0.0f : sc;
-  if (out0 && tid == 0) xs[0] = xsm;
+  // lane (m, g) scales output column m by row min(m, MR - 1)'s scale
+  float xsm = zr[0] ? 0.0f : sc[0];
+#pragma unroll
+  for (int r = 1; r < MR; ++r)
+    if (r == MR - 1 ? r16 >= r : r16 == r) xsm = zr[r] ? 0.0f : sc[r];
+  if (out0 && tid < M) {
+    float v = zr[0] ? 0.0f : sc[0];
+#pragma unroll
+    for (int r = 1; r < MR; ++r)
+      if (tid == r) v = zr[r] ? 0.0f : sc[r];
+    xs[tid] = v;
+  }
 
   // 4. the units: weight block in LDS, the codes broadcast per step, MFMAs
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -1653,7 +1717,12 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
         dma(wave + c * NW);
       }
       wait_vmcnt<0>();
-      x1_unit<XF, WF, ACC>(acc0, acc1, x1[c], region, a_even, a_odd, i_row, r7, std::make_integer_sequence<int, 8>{});
+      if constexpr (MR == 1)
+        x1_unit<XF, WF, ACC>(acc0, acc1, x1[c][0], region, a_even, a_odd, i_row, r7,
+                             std::make_integer_sequence<int, 8>{});
+      else
+        xl_unit<XF, WF, ACC>(acc0, acc1, xw + (c * MR + min(r16, MR - 1)) * kCodeRow + 16 * lg, region, a_even, a_odd,
+                             i_row, r7, std::make_integer_sequence<int, 8>{});
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -1672,21 +1741,38 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
       y[2] += bf16_to_f32(b2.y & 0xFFFFu);
       y[3] += bf16_to_f32(b2.y >> 16);
     }
-    if (r16 == 0) store4<OUT>(out, N, 0, n, y);
+    if (r16 < M) store4<OUT>(out, N, r16, n, y);
   }
 }
 
-// Fused path of the bf16-activation entry point: one activation row,
-// K a multiple of 1024 up to 16384.
-inline bool fused_decode_ok(int64_t m, int64_t k) {
-  return m == 1 && k % kUnitK == 0 && k <= 8 * kFusedMaxUnitsPerWave * kUnitK;
+// Fused path of the bf16-activation entry point, where one launch beats
+// quantization + linear layer (measured against them on the Llama shapes,
+// N 4096 .. 14336, K 4096 .. 14336, 1 .. 4 rows: one launch 0.9 .. 2.1 us
+// faster where chosen).  Every workgroup quantizes all the rows it uses, so
+// the redundant casts grow with rows x workgroups; above K = 4096 the 8
+// wavefronts' weight blocks and activation chunks take most of the LDS, one
+// workgroup per CU.
+//  - 1 or 2 rows, K a multiple of 1024: up to 4096 always; up to 16384 while
+//    the workgroups (16 weight rows each) fit the CUs once (at N = 6144,
+//    K = 8192 two launches were 1.6 .. 2.8 us faster);
+//  - 3 or 4 rows: K up to 4096 and at most 1.5 workgroups per CU (at 4096
+//    one launch is 0.7 us faster, at 6144 even, at 14336 and at K = 8192 two
+//    launches are faster).
+inline int fused_rows(int64_t m) { return m == 1 ? 1 : m == 2 ? 2 : 4; }
+inline bool fused_decode_ok(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > 4 || k % kUnitK != 0) return false;
+  const int64_t wgs = n / 16, cus = device_cus();
+  if (m <= 2) return k <= 4 * kUnitK || (k <= 16 * kUnitK && wgs <= cus);
+  return k <= 4 * kUnitK && 2 * wgs <= 3 * cus;
 }
 
-template <int XF, int WF, int OUT, int ACC, int NWMAX>
+template <int XF, int WF, int OUT, int ACC, int NWMAX, int MR>
 hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, int nw,
                                hipStream_t stream) {
-  constexpr unsigned lds = NWMAX * kUnitLds + NWMAX * (NWMAX == 8 ? kFusedMaxUnitsPerWave : 1) * 2048 + 4 * NWMAX;
-  auto kern = linear_decode_unit_fused1_kernel<XF, WF, OUT, ACC, NWMAX>;
+  constexpr int UPW = NWMAX == 8 ? kFusedMaxUnitsPerWave : 1;
+  constexpr unsigned lds = NWMAX * kUnitLds + NWMAX * UPW * MR * 2048 + 4 * NWMAX * MR;
+  static_assert(lds <= 160 * 1024, "LDS");
+  auto kern = linear_decode_unit_fused1_kernel<XF, WF, OUT, ACC, NWMAX, MR>;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1695,18 +1781,27 @@ hipError_t run_decode_fused_nw(const uint16_t* x, uint8_t* xq, float* xs, const 
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.n / 16)), dim3(64 * nw), lds, stream, x, xq, xs, a.values, a.meta, a.ws,
-                     a.bias, a.out, (int)a.n, (int)a.k, a.ws_stride);
+                     a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.ws_stride);
   return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT, int ACC, int MR>
+hipError_t run_decode_fused_rows(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
+  // the static LDS is sized for the smallest of 2, 4, 8 wavefronts that covers
+  // the units, so small K keeps several workgroups per CU
+  const int nw = unit_waves(a.k);
+  if (nw <= 2) return run_decode_fused_nw<XF, WF, OUT, ACC, 2, MR>(x, xq, xs, a, nw, stream);
+  if (nw <= 4) return run_decode_fused_nw<XF, WF, OUT, ACC, 4, MR>(x, xq, xs, a, nw, stream);
+  if constexpr (MR < 4) return run_decode_fused_nw<XF, WF, OUT, ACC, 8, MR>(x, xq, xs, a, nw, stream);
+  return hipErrorInvalidValue;  // 3 or 4 rows: fused_decode_ok keeps K <= 4096
 }
 
 template <int XF, int WF, int OUT, int ACC>
 hipError_t run_decode_fused(const uint16_t* x, uint8_t* xq, float* xs, const LinearArgs& a, hipStream_t stream) {
-  // the static LDS is sized for the smallest of 2, 4, 8 wavefronts that covers
-  // the units, so small K keeps several workgroups per CU
-  const int nw = unit_waves(a.k);
-  if (nw <= 2) return run_decode_fused_nw<XF, WF, OUT, ACC, 2>(x, xq, xs, a, nw, stream);
-  if (nw <= 4) return run_decode_fused_nw<XF, WF, OUT, ACC, 4>(x, xq, xs, a, nw, stream);
-  return run_decode_fused_nw<XF, WF, OUT, ACC, 8>(x, xq, xs, a, nw, stream);
+  const int mr = fused_rows(a.m);
+  if (mr == 1) return run_decode_fused_rows<XF, WF, OUT, ACC, 1>(x, xq, xs, a, stream);
+  if (mr == 2) return run_decode_fused_rows<XF, WF, OUT, ACC, 2>(x, xq, xs, a, stream);
+  return run_decode_fused_rows<XF, WF, OUT, ACC, 4>(x, xq, xs, a, stream);
 }
 
 template <int XF, int WF, int OUT, int ACC>
@@ -1857,7 +1952,7 @@ hipError_t launch_linear_dynamic(const uint16_t* x, uint8_t* xq, float* xs, cons
                                  hipStream_t stream) {
   const int dflt = linear_default_algo(a.m, a.n, a.k);
   if (algo < 0) algo = dflt;
-  if (!fused_decode_ok(a.m, a.k) || (algo & 0xFF) != (dflt & 0xFF)) {
+  if (!fused_decode_ok(a.m, a.n, a.k) || (algo & 0xFF) != (dflt & 0xFF)) {
     // two launches: the row-wise quantization, then the linear layer
     hipError_t e = launch_quantize(x, a.m, a.k, a.x_fmt, xq, xs, stream);
     if (e != hipSuccess) return e;

@@ -9,9 +9,11 @@
 // and no cross-workgroup step exist at all.
 //
 // The per-element division x / scale is done as a multiplication by the
-// row's reciprocal with an exactness check (cast8): the IEEE
-// division runs only for the rare elements whose FP8 rounding the check cannot
-// settle, so the codes are those of the plain division.
+// row's reciprocal with one fma correction (cast8; for scales from 2^-80 up,
+// checked to give the codes of the plain division for every bf16 input),
+// below that scale with an exactness check that sends the rare elements it
+// cannot settle to the IEEE division; either way the codes are those of the
+// plain division.
 //
 // Layout: one 64-lane wavefront owns one row.  Lane l holds 16-byte chunks
 // (8 bf16) l, l+64, l+128, ... of its row in registers between the amax sweep

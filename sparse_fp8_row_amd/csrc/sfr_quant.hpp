@@ -47,42 +47,65 @@ __device__ __forceinline__ bool quotient_settled(float x, float q) {
   return ((b >= kMinNormal) & (b < 0x7F800000u) & far) | (x == 0.0f);
 }
 
+// Smallest scale for which cast8 forms the quotients with one fma
+// correction (below it: the tested product, see cast8).
+constexpr float kFmaQuotientMinScale = 0x1p-80f;
+
 // 8 bf16 -> 8 FP8 bytes.  `scale` > 0, `rcp` = fl32(1 / scale): the codes of
 // fl32(x / scale) (IEEE binary32 division), clamped to +/-fmax and rounded to
-// nearest even by the hardware converter.
+// nearest even by the hardware converter.  The row's elements satisfy
+// |x| <= amax with scale = fl32(amax / fmax).
 //
-// The quotients are formed as q = fl32(x * rcp), which differs from x / scale
-// by at most 2^-23 relative, so fl32(x / scale) lies within a few binary32
-// steps of q.  An FP8 code only changes where the value crosses the midpoint
-// between two FP8 neighbours; in the FP8 normal range that midpoint has the
-// low 20 (e4m3) or 21 (e5m2) bits of the binary32 pattern equal to 0x80000 /
-// 0x100000.  When q's low bits are more than 8 steps from it, q and
-// fl32(x / scale) round to the same code (at binade edges the low bits are
-// near 0 or all ones, far from the midpoint).  Zero divides to a signed zero
-// (taken as is: rcp is infinite when scale is below 2^-128).  An element the
-// test cannot settle -- near a midpoint, in the FP8 subnormal
-// range, or not finite -- takes the IEEE division (one branch per 8 elements).
+// From scale 2^-80 up the quotient is q0 = fl32(x * rcp), corrected once:
+// q = fma(-fma(q0, scale, -x), rcp, q0) (the residual negated twice, so that
+// x = -0 keeps its sign).  q is not always fl32(x / scale) -- it can differ
+// by a unit in the last place -- but it always gives the same FP8 code: this
+// was checked by enumerating every bf16 amax and every bf16 x with
+// |x| <= amax, for both formats (about 2.1e9 pairs; codes first differ at
+// scales below 2^-106).
+//
+// Below 2^-80 the quotients are formed as q = fl32(x * rcp), which differs
+// from x / scale by at most 2^-23 relative, so fl32(x / scale) lies within a
+// few binary32 steps of q.  An FP8 code only changes where the value crosses
+// the midpoint between two FP8 neighbours; in the FP8 normal range that
+// midpoint has the low 20 (e4m3) or 21 (e5m2) bits of the binary32 pattern
+// equal to 0x80000 / 0x100000.  When q's low bits are more than 8 steps from
+// it, q and fl32(x / scale) round to the same code (at binade edges the low
+// bits are near 0 or all ones, far from the midpoint).  Zero divides to a
+// signed zero (taken as is: rcp is infinite when scale is below 2^-128).  An
+// element the test cannot settle -- near a midpoint, in the FP8 subnormal
+// range, or not finite -- takes the IEEE division (one branch per 8
+// elements).
 template <int FMT>
 __device__ __forceinline__ uint2 cast8(uint4 c, float scale, float rcp) {
   constexpr float fmax = Fp8<FMT>::fmax;
   uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float x[8], t[8];
-  bool settled = true;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
     x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
+  if (__builtin_expect(scale >= kFmaQuotientMinScale, 1)) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // a zero keeps its sign (x * rcp would give NaN when rcp is infinite)
-    t[i] = x[i] == 0.0f ? x[i] : x[i] * rcp;
-    settled &= quotient_settled<FMT>(x[i], t[i]);
-  }
-  if (__builtin_expect(!settled, 0)) {
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = x[i] * rcp;
+      const float rn = __builtin_fmaf(q0, scale, -x[i]);
+      t[i] = __builtin_fmaf(-rn, rcp, q0);
+    }
+  } else {
+    bool settled = true;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (!quotient_settled<FMT>(x[i], t[i])) t[i] = x[i] / scale;
+    for (int i = 0; i < 8; ++i) {
+      // a zero keeps its sign (x * rcp would give NaN when rcp is infinite)
+      t[i] = x[i] == 0.0f ? x[i] : x[i] * rcp;
+      settled &= quotient_settled<FMT>(x[i], t[i]);
+    }
+    if (!settled) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (!quotient_settled<FMT>(x[i], t[i])) t[i] = x[i] / scale;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(t[i], -fmax), fmax);

@@ -1,14 +1,16 @@
 """GPU parity of sparse_fp8_rowwise_linear_dynamic (activation quantization
-fused into the decode GEMM launch for one activation row; two launches,
+fused into the decode GEMM launch for 1 to 4 activation rows; two launches,
 quantization then the linear layer, for other shapes).
 
 The codes and scales it writes are compared bit for bit with the oracle's
 row-wise quantization, the output with the oracle's linear layer (same rules
-as the row-wise tests), on every fused shape class (K from one 1024-k unit
-to 16384, one and two units per wavefront, uneven unit counts, grids smaller
-and larger than the chip holds at once, row and tensor weight scales, an
-all-zero row) and on the two-launch path (row counts 2 .. 17 including odd
-ones, K not a multiple of 1024 or above 16384, all-zero rows).
+as the row-wise tests), on every fused shape class (1, 2, 3 and 4 rows; K
+from one 1024-k unit to 16384 with 1 or 2 rows, to 4096 with 3 or 4; one and
+two units per wavefront, uneven unit counts, grids smaller and larger than
+the chip holds at once, row and tensor weight scales, all-zero rows) and on
+the two-launch path (row counts 3 .. 17 including odd ones, K not a multiple
+of 1024, K above the fused limit, 3 or 4 rows over many workgroups, all-zero
+rows).
 """
 import sys
 
@@ -64,10 +66,13 @@ def run_case(gpu, case, wscale="row", seed_shift=0):
         assert r["bad"] == 0, r
 
 
-# (m, n, k): fused shapes (n/16 workgroups: 16 .. 896, more than the chip's 256 CUs;
-# K/1024 units over up to 8 wavefronts: 1, 2, 4, 5 x (2,2,2,2,1), 7 x 2, 8 x 2)
+# (m, n, k): fused shapes (n/16 workgroups: 16 .. 896, more than the chip's 256 CUs
+# at K <= 4096; K/1024 units over up to 8 wavefronts: 1, 2, 3, 4, 5 x (2,2,2,2,1),
+# 7 x 2, 8 x 2)
 FUSED = [(1, 4096, 4096), (1, 1040, 1024), (1, 14336, 4096), (1, 256, 2048), (1, 2048, 9216), (1, 512, 14336),
-         (1, 4096, 16384)]
+         (1, 4096, 16384), (2, 4096, 4096), (2, 1040, 1024), (2, 512, 14336), (2, 1024, 16384), (2, 4096, 9216),
+         (2, 14336, 4096), (3, 1024, 2048), (3, 256, 3072), (3, 6144, 4096), (4, 4096, 4096), (4, 1040, 1024),
+         (4, 6144, 3072), (4, 512, 3072)]
 
 
 @pytest.mark.parametrize("shape", FUSED, ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
@@ -98,14 +103,17 @@ def test_dynamic_fused_zero_row(gpu):
     assert np.array_equal(host_bf16_bits(y)[0], bb)
 
 
-def test_dynamic_zero_rows_multi(gpu):
-    # several rows with all-zero rows (both zero signs) among them
+@pytest.mark.parametrize("m,zero_rows", [(6, (2, 5)), (4, (1, 3)), (2, (0,))])
+def test_dynamic_zero_rows_multi(gpu, m, zero_rows):
+    # several rows with all-zero rows (both zero signs) among them (4 and 2
+    # rows: one launch, 6: two)
     n, k = 4096, 3072
-    case = sfr_inputs.Case("dyn_zero_m", 14, 6, n, k, bias=True)
+    case = sfr_inputs.Case("dyn_zero_m", 14, m, n, k, bias=True)
     xb = sfr_inputs.draw_x(case)
-    xb[2] = 0
-    xb[2, 1::3] = 0x8000
-    xb[5] = 0x8000
+    za, zb = zero_rows[0], zero_rows[-1]
+    xb[za] = 0
+    xb[za, 1::3] = 0x8000
+    xb[zb] = 0x8000
     wb = sfr_inputs.draw_w(case)
     bb = sfr_inputs.draw_bias(case)
     pw = gpu.prepare_weight(dev_bf16(wb), torch.float8_e4m3fn)
@@ -118,15 +126,19 @@ def test_dynamic_zero_rows_multi(gpu):
     r = check_bf16(host_bf16_bits(y), oracle.linear(oxq, E4, oxs, ov, om, E4, ows, bias=bb))
     say(f"  zero rows {r}")
     assert r["bad"] == 0, r
-    assert np.array_equal(host_bf16_bits(y)[2], bb) and np.array_equal(host_bf16_bits(y)[5], bb)
+    assert np.array_equal(host_bf16_bits(y)[za], bb) and np.array_equal(host_bf16_bits(y)[zb], bb)
 
 
-# shapes that take the two-launch path: m > 1 (16 or 32 weight rows per
-# workgroup in the linear layer), k not a multiple of 1024, k > 16384
+# shapes that take the two-launch path: m > 4 (16 or 32 weight rows per
+# workgroup in the linear layer), k not a multiple of 1024, k above 16384
+# (above 4096 with 3 or 4 rows), k above 4096 with more workgroups than CUs,
+# 3 or 4 rows over more than 1.5 workgroups per CU
 @pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 6144, 16384), (1, 4096, 640),
-                                   (1, 256, 17408), (3, 1024, 640), (2, 4096, 4096), (4, 4096, 4096),
-                                   (16, 4096, 4096), (3, 1024, 2048), (7, 4096, 14336), (16, 4096, 14336),
-                                   (16, 14336, 4096), (8, 6144, 4096), (13, 6144, 9216), (5, 2080, 1024)],
+                                   (1, 256, 17408), (3, 1024, 640), (2, 4096, 17408), (4, 4096, 9216),
+                                   (16, 4096, 4096), (3, 1024, 14336), (7, 4096, 14336), (16, 4096, 14336),
+                                   (16, 14336, 4096), (8, 6144, 4096), (13, 6144, 9216), (5, 2080, 1024),
+                                   (4, 14336, 4096), (3, 8192, 1024), (2, 6144, 9216), (4, 2048, 8192),
+                                   (1, 6144, 8192)],
                          ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
 def test_dynamic_two_launch(gpu, shape):
     m, n, k = shape
@@ -134,14 +146,15 @@ def test_dynamic_two_launch(gpu, shape):
 
 
 def test_dynamic_back_to_back(gpu):
-    # several calls in a row on one stream (fused and two-launch), each checked
+    # several calls in a row on one stream (fused with 1 to 4 rows and
+    # two-launch), each checked
     n, k = 4096, 4096
     case_w = sfr_inputs.Case("dyn_seq", 11, 16, n, k, bias=True)
     wb = sfr_inputs.draw_w(case_w)
     pw = gpu.prepare_weight(dev_bf16(wb), torch.float8_e4m3fn)
     ov, om, ows, _ = oracle.prepare_weight(wb, E4)
     outs, refs = [], []
-    for i, m in enumerate((1, 4, 1, 9)):
+    for i, m in enumerate((1, 4, 1, 9, 2, 3)):
         case = sfr_inputs.Case("dyn_seq", 20 + i, m, n, k)
         xb = sfr_inputs.draw_x(case)
         y, xq, xs = gpu.sparse_fp8_rowwise_linear_dynamic(dev_bf16(xb), pw.values, pw.meta, pw.scale)
