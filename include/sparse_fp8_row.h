@@ -269,10 +269,14 @@ sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const flo
  * quantized dynamically, per call).  xq and xs receive exactly the bytes
  * quantize_rowwise_fp8 writes; out is as sparse_fp8_scaled_linear.
  *
- * For one activation row (m == 1) with k a multiple of 1024 up to 16384,
- * both steps run in ONE launch: every workgroup quantizes the row itself (no
- * workgroup waits for another).  Other shapes take two launches
- * (quantization, then the linear layer).
+ * For 1 to 4 activation rows with k a multiple of 1024, both steps run in
+ * ONE launch where that is faster: every workgroup quantizes the rows itself
+ * (no workgroup waits for another), so the redundant work grows with rows x
+ * workgroups.  One launch is taken for 1 or 2 rows with k up to 4096, or up
+ * to 16384 while n / 16 does not exceed the device's CU count; for 3 or 4
+ * rows with k up to 4096 and n / 16 at most 1.5 x the CU count.  Other shapes
+ * take two launches (quantization, then the linear layer).  Both paths write
+ * the same bytes.
  *
  *   x      [m, k] bf16 bits, device, read.
  *   xq     [m, k] FP8 bytes (format x_dt), device, written.
