@@ -168,21 +168,10 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
   const int a_rd0 = r16 * 128 + 16 * (g ^ (r16 & 7)), a_rd1 = r16 * 128 + 16 * ((4 + g) ^ (r16 & 7));
   uint8_t* const mine = wbuf[wave];
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  // the block columns of a group (lane u holds block u's) are loaded one
-  // group ahead, so the activation addresses are ready before the group's
-  // global->LDS loads go out (a wait for an ordinary load would also wait
-  // for those)
-  int cv = j0 + wave < j1 ? col[min(j0 + wave + NW * min(lane, U - 1), j1 - 1)] : 0;
   for (int jb = j0 + wave; jb < j1; jb += NW * U) {
     const int live = min(U, (j1 - jb + NW - 1) / NW);  // blocks of this group (uniform)
     v4i a[U][2], b[U][2];
-    const uint8_t* xb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // a corrupt index is clamped so the activation read stays inside x
-      const int64_t bc = min((int64_t)(uint32_t)__builtin_amdgcn_readlane(cv, u), kmax);
-      xb[u] = xrow + bc * (BS * 2);
-    }
+    // the weight slices first: their addresses need the block index only
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < live) {
@@ -192,15 +181,21 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
           __builtin_amdgcn_global_load_lds((void*)(vb + h * 8 * (BS * 2)), (void*)(mine + u * 2048 + h * 1024), 16, 0, 0);
       }
     }
+    // then the block columns, as uniform (scalar) loads: waiting for them
+    // does not wait for the slices, which stream meanwhile; then the
+    // activation at those columns (a corrupt index is clamped so the read
+    // stays inside x)
+    int64_t bc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bc[u] = col[__builtin_amdgcn_readfirstlane(jb + NW * min(u, live - 1))];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < live) {
+        const uint8_t* xb = xrow + min((int64_t)(uint32_t)bc[u], kmax) * (BS * 2);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) b[u][s] = *reinterpret_cast<const v4i*>(xb[u] + 64 * s);
+        for (int s = 0; s < 2; ++s) b[u][s] = *reinterpret_cast<const v4i*>(xb + 64 * s);
       }
     }
-    // the next group's block columns (clamped into this block row)
-    cv = col[min(jb + NW * U + NW * min(lane, U - 1), j1 - 1)];
     // every load has landed (the activation loads and the global->LDS ones
     // share the counter); then the slices' operand chunks
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters at maximum (gfx9 encoding)
