@@ -160,6 +160,14 @@ def rows_bits(kind, rows, cols, seed):
         x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-120, 120, (rows, 1)))
     elif kind == "tiny":
         x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-133, -118, (rows, 1)))
+    elif kind == "edge":
+        # row maxima at fmax * 2^-80 (e4m3 rows even, e5m2 rows odd) and one
+        # bf16 step below / above it: the scale lands just under, on and over
+        # 2^-80, where the kernels' quotient method changes
+        base = np.where(np.arange(rows) % 2 == 0, 1.75 * 2.0 ** -72, 1.75 * 2.0 ** -65)
+        top = base * np.array([1.7421875, 1.75, 1.7578125])[(np.arange(rows) // 2) % 3] / 1.75
+        x = rng.uniform(-1.0, 1.0, (rows, cols)) * top[:, None]
+        x[np.arange(rows), rng.integers(0, cols, rows)] = top * np.where(rng.random(rows) < 0.5, -1.0, 1.0)
     bits = sfr_inputs.to_bf16_bits(x)
     z = rng.random((rows, cols)) < 0.02
     bits[z] = np.where(rng.random(int(z.sum())) < 0.5, 0x8000, 0x0000)

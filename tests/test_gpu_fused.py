@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import sfr_inputs
-from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, FP8_TORCH
+from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, rows_bits, FP8_TORCH
 
 pytestmark = pytest.mark.gpu
 
@@ -169,9 +169,10 @@ def test_dynamic_back_to_back(gpu):
         assert r["bad"] == 0, r
 
 
-def test_dynamic_matches_two_step_path(gpu):
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_dynamic_matches_two_step_path(gpu, m):
     # the fused call gives the same bytes as quantize_rowwise_fp8 + sparse_fp8_rowwise_linear
-    case = sfr_inputs.Case("dyn_eq", 12, 1, 2048, 4096, x_fmt=E5, w_fmt=E5, bias=True)
+    case = sfr_inputs.Case("dyn_eq", 12, m, 2048, 4096, x_fmt=E5, w_fmt=E5, bias=True)
     xb = dev_bf16(sfr_inputs.draw_x(case))
     pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)), torch.float8_e5m2)
     b = dev_bf16(sfr_inputs.draw_bias(case))
@@ -182,4 +183,30 @@ def test_dynamic_matches_two_step_path(gpu):
     torch.cuda.synchronize()
     assert np.array_equal(host_bytes(xq), host_bytes(xq2))
     assert np.array_equal(host_f32(xs).view(np.uint32), host_f32(xs2).view(np.uint32))
+    assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+@pytest.mark.parametrize("kind", ["wide", "tiny", "edge"])
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_dynamic_fused_extreme_rows(gpu, m, kind, fmt):
+    # row maxima over the whole exponent range, below 2^-118, and around
+    # scale 2^-80 (both quotient methods of the cast): codes and scales bit
+    # for bit against the oracle, the output bit for bit against the two-step
+    # path (the products of such rows are subnormal in binary32, so the
+    # output is compared with the same kernel arithmetic, not the oracle)
+    n, k = 1024, 2048
+    say(f"dynamic extreme {kind} m={m} fmt={fmt}")
+    xb = rows_bits(kind, m, k, 40 + 7 * m)
+    case = sfr_inputs.Case("dyn_x", 16, m, n, k, bias=True)
+    pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)), torch.float8_e4m3fn)
+    b = dev_bf16(sfr_inputs.draw_bias(case))
+    x = dev_bf16(xb)
+    y, xq, xs = gpu.sparse_fp8_rowwise_linear_dynamic(x, pw.values, pw.meta, pw.scale, b, act_dtype=FP8_TORCH[fmt])
+    xq2, xs2 = gpu.quantize_rowwise_fp8(x, FP8_TORCH[fmt])
+    y2 = gpu.sparse_fp8_rowwise_linear(xq2, xs2, pw.values, pw.meta, pw.scale, b)
+    torch.cuda.synchronize()
+    oxq, oxs = oracle.quantize_rows(xb, fmt)
+    assert np.array_equal(host_bytes(xq), oxq)
+    assert np.array_equal(host_f32(xs).view(np.uint32), oxs.view(np.uint32))
     assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))

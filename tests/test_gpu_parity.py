@@ -48,7 +48,7 @@ QSHAPES = [(1, 8), (3, 256), (17, 4096), (64, 4104), (5, 16384), (4, 16392), (13
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
-@pytest.mark.parametrize("kind", ["normal", "student", "wide", "tiny"])
+@pytest.mark.parametrize("kind", ["normal", "student", "wide", "tiny", "edge"])
 @pytest.mark.parametrize("shape", QSHAPES)
 def test_quantize_bit_exact(gpu, fmt, kind, shape):
     rows, cols = shape

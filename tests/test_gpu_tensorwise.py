@@ -40,7 +40,7 @@ TSHAPES = [(1, 8), (3, 256), (17, 4096), (64, 4104), (130, 512), (9, 14336), (20
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
-@pytest.mark.parametrize("kind", ["normal", "student", "wide", "tiny", "zero"])
+@pytest.mark.parametrize("kind", ["normal", "student", "wide", "tiny", "edge", "zero"])
 @pytest.mark.parametrize("shape", TSHAPES)
 def test_tensorwise_quantize_bit_exact(gpu, fmt, kind, shape):
     rows, cols = shape
