@@ -52,7 +52,7 @@
 //    #1734 ("promote blocksparse from prototype ...").
 //    linear_decode_kernel streams the weight into registers instead (any K
 //    that is a multiple of 128), and linear_decode_unit_fused1_kernel also
-//    quantizes a single bf16 activation row itself.
+//    quantizes 1 to 4 bf16 activation rows itself.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -1500,24 +1500,29 @@ hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode from the bf16 activation, one row: quantization fused in front of
-// the unit kernel.
+// Decode from the bf16 activation, 1 to 4 rows: quantization fused in front
+// of the unit kernel.
 // ---------------------------------------------------------------------------
-// The single-row form of linear_decode_unit_kernel (same units, LDS regions,
-// row broadcast of the activation and reduction) that first quantizes the
-// bf16 row itself, exactly as quantize_rowwise_fp8 does.  Every wavefront
-// starts its first unit's weight loads, then loads the bf16 values of its
-// units that its lanes will hold as codes (lane (r, g): the 16 elements
-// 8 (r >> 1) + 4 (r & 1) + g of a unit, in 16-byte chunks of codes).  The
-// compiler makes the first use of those values wait for the weight loads as
-// well (ordinary and global->LDS loads pending together count as unordered,
-// and any LDS access waits for pending global->LDS loads), so the row
-// maximum (over lanes by DPP, over wavefronts through LDS; every wavefront
-// reading the whole row instead measured slower), the scale, its reciprocal
-// and cast8 run once the weight block has landed: a few hundred cycles after
-// the stream, against a second launch.  Workgroup 0 also
-// writes the codes and the scale to xq / xs.  A wavefront holds at most 2
-// units of the activation (K <= 16384 with 8 wavefronts).
+// linear_decode_unit_kernel's units, LDS regions and reduction, for MR = 1, 2
+// or 4 activation rows that the kernel first quantizes itself, exactly as
+// quantize_rowwise_fp8 does.  Every wavefront puts the bf16 chunks of its
+// units (each row's, for lane (r, g) the 16 elements 8 (r >> 1) + 4 (r & 1)
+// + g of a unit) and then its first unit's weight block in flight, all as
+// global->LDS loads (fused_first_loads), and reads the chunks back once only
+// the weight loads are pending.  Each row's maximum (over lanes by DPP, over
+// wavefronts through LDS; every wavefront reading the whole row instead
+// measured slower), the scales, their reciprocals and cast8 follow; the LDS
+// exchange waits for the weight block too (any LDS access waits for pending
+// global->LDS loads), so the casts run a few hundred cycles after the
+// stream, against a second launch.  With one row the codes stay in
+// registers and each step broadcasts its operand across the 16-lane rows
+// (x1_unit); with several, each row's codes go back to the wavefront's
+// staging area and each lane reads its own row's operand there (xl_unit).
+// Workgroup 0 also writes the codes and the scales to xq / xs.  Every
+// workgroup repeats the casts of all its rows, which is why the host takes
+// this path only for few rows and workgroups (fused_decode_ok).  A
+// wavefront holds at most 2 units of the activation (K <= 16384 with 8
+// wavefronts).
 constexpr int kFusedMaxUnitsPerWave = 2;
 constexpr int kCodeRow = kUnitK + 16;  // LDS stride of a row's codes (several rows)
 
