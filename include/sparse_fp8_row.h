@@ -338,7 +338,8 @@ sfr_status sparse_fp8_rowwise_linear_dynamic_algo(const uint16_t* x, sfr_fp8_t x
  * Configurations: 0 decode_lds (m <= 64, k % 1024 == 0), 1 decode_reg
  * (m <= 16), 2 tiled_64x64, 3 tiled_128x128, 4 tiled_256x256,
  * 5 wide_256x256 (k >= 512, only with SFR_ALGO_ACC_F8), 6 decode_lds_32
- * (m <= 64, k % 1024 == 0, n % 32 == 0).
+ * (m <= 64, k % 1024 == 0, n % 32 == 0), 7 tiled_256x128 (tiles of 256
+ * output columns n by 128 rows m).
  */
 #define SFR_ALGO_DEFAULT (-1)
 #define SFR_ALGO_ACC_F8 0x100

@@ -1847,6 +1847,11 @@ hipError_t run_algo(const LinearArgs& a, int cfg, hipStream_t stream) {
       if (persistent_ok(a, 256)) return run_persistent<XF, WF, OUT, ACC, 256, 256, 4, 2, 4, 8, 1, 1>(a, stream);
       return run_tiled<XF, WF, OUT, ACC, 256, 256, 4, 2, 8, 2, 2, 1, 8, 1>(a, stream);
     case ALGO_DECODE_LDS_32: return run_decode_unit<XF, WF, OUT, ACC, 2>(a, stream);
+    case ALGO_TILED_256x128:
+      // the persistent kernel with half-height tiles: for shapes whose
+      // 256 x 256 tiles leave most CUs idle
+      if (persistent_ok(a, 256)) return run_persistent<XF, WF, OUT, ACC, 256, 128, 4, 2, 4, 8, 1, 1>(a, stream);
+      return run_tiled<XF, WF, OUT, ACC, 256, 128, 4, 2, 8, 2, 2, 1, 8, 1>(a, stream);
     default:  // ALGO_WIDE_256: FP8 accumulation only (checked by linear_algo_supported)
       if constexpr (ACC == ACC_F8) return run_wide<XF, WF, OUT, 8>(a, stream);
       else return hipErrorInvalidValue;
@@ -1867,9 +1872,10 @@ hipError_t run_out(const LinearArgs& a, int cfg, int acc, hipStream_t stream) {
 
 const char* linear_algo_name(int algo) {
   static const char* const names[2][ALGO_COUNT] = {
-      {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128", "tiled_256x256", nullptr, "decode_lds_32"},
+      {"decode_lds", "decode_reg", "tiled_64x64", "tiled_128x128", "tiled_256x256", nullptr, "decode_lds_32",
+       "tiled_256x128"},
       {"decode_lds+f8acc", "decode_reg+f8acc", "tiled_64x64+f8acc", "tiled_128x128+f8acc", "tiled_256x256+f8acc",
-       "wide_256x256+f8acc", "decode_lds_32+f8acc"}};
+       "wide_256x256+f8acc", "decode_lds_32+f8acc", "tiled_256x128+f8acc"}};
   if (algo < 0 || (algo & ~(ALGO_ACC_F8_FLAG | 0xFF)) != 0) return nullptr;
   const int cfg = algo & 0xFF;
   const bool f8 = (algo & ALGO_ACC_F8_FLAG) != 0;
@@ -1886,7 +1892,8 @@ bool linear_algo_supported(int algo, int64_t m, int64_t n, int64_t k) {
     case ALGO_DECODE_REG: return m <= 16;
     case ALGO_TILED_64:
     case ALGO_TILED_128:
-    case ALGO_TILED_256: return true;
+    case ALGO_TILED_256:
+    case ALGO_TILED_256x128: return true;
     case ALGO_WIDE_256: return (algo & ALGO_ACC_F8_FLAG) && k >= 4 * KSTEP;
     case ALGO_DECODE_LDS_32: return m <= 64 && k % kUnitK == 0 && n % 32 == 0;
     default: return false;
@@ -1922,8 +1929,14 @@ static int default_config(int64_t m, int64_t n, int64_t k) {
   // from two full rounds on.
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+  const int64_t t2x1 = ((m + 127) / 128) * ((n + 255) / 256);
   const int64_t r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
   if (t256 >= 2 * cus || 3 * r256 <= 2 * r128) return ALGO_TILED_256;
+  // One round of 256(n) x 128(m) persistent tiles covering 3/4 to all of the
+  // CUs: 11-15% faster than the 128x128 tiles (measured on the Llama shapes
+  // at M = 512 (N = 14336), 1024 (N = 6144) and 2048 (N = 4096, K = 4096 and
+  // 14336)); with fewer tiles too many CUs idle.
+  if (4 * t2x1 >= 3 * cus && t2x1 <= cus) return ALGO_TILED_256x128;
   if (t128 >= cus) return ALGO_TILED_128;
   return ALGO_TILED_64;
 }

@@ -182,17 +182,17 @@ def test_prune_validation(lib):
 def test_linear_algos(lib):
     names = [lib.sfr_linear_algo_name(i) for i in range(lib.sfr_linear_algo_count())]
     assert names == [b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128", b"tiled_256x256",
-                     None, b"decode_lds_32"]
+                     None, b"decode_lds_32", b"tiled_256x128"]
     f8 = [lib.sfr_linear_algo_name(i | F8) for i in range(lib.sfr_linear_algo_count())]
     assert f8 == [n + b"+f8acc" for n in (b"decode_lds", b"decode_reg", b"tiled_64x64", b"tiled_128x128",
-                                          b"tiled_256x256", b"wide_256x256", b"decode_lds_32")]
-    for a in (7, -1, 5, 7 | F8, 0x200, 0x300, 1 << 20):
+                                          b"tiled_256x256", b"wide_256x256", b"decode_lds_32", b"tiled_256x128")]
+    for a in (8, -1, 5, 8 | F8, 0x200, 0x300, 1 << 20):
         assert lib.sfr_linear_algo_name(a) is None and lib.sfr_linear_algo_valid(a) == 0, a
-    assert all(lib.sfr_linear_algo_valid(a) == 1 for a in (0, 4, 6, 0 | F8, 5 | F8, 6 | F8))
+    assert all(lib.sfr_linear_algo_valid(a) == 1 for a in (0, 4, 6, 7, 0 | F8, 5 | F8, 6 | F8, 7 | F8))
     sup = lambda a, m, n, k: lib.sfr_linear_algo_supported(a, m, n, k)
     # each accumulation supports the same shapes per configuration (the
     # pipelined kernel only with FP8 accumulation)
-    for a in (0, 1, 2, 3, 4, 6):
+    for a in (0, 1, 2, 3, 4, 6, 7):
         for shape in ((64, 4096, 4096), (65, 4096, 4096), (4, 4096, 640), (16, 4096, 640), (17, 4096, 640),
                       (5000, 4096, 256), (4, 4112, 1024)):
             assert sup(a, *shape) == sup(a | F8, *shape), (a, shape)
@@ -203,18 +203,20 @@ def test_linear_algos(lib):
     assert sup(0, 4, 4096, 640) == 0 and sup(0, 4, 4096, 17408) == 1        # unit decode: k % 1024, any K
     assert sup(6, 4, 4096, 1024) == 1 and sup(6, 4, 4112, 1024) == 0        # 32 rows per workgroup: n % 32
     assert sup(1, 16, 4096, 640) == 1 and sup(1, 17, 4096, 640) == 0
-    assert all(sup(a, 5000, 4096, 256) == 1 for a in (2, 3, 4))
-    assert sup(2, 4, 100, 256) == 0 and sup(7, 4, 128, 256) == 0           # bad n, unknown id
+    assert all(sup(a, 5000, 4096, 256) == 1 for a in (2, 3, 4, 7))
+    assert sup(2, 4, 100, 256) == 0 and sup(8, 4, 128, 256) == 0           # bad n, unknown id
     # the built-in choice
     d = lib.sfr_linear_default_algo
     assert d(1, 4096, 4096) == 0 and d(16, 4096, 14336) == 0 and d(16, 4096, 17408) == 0
     assert d(1, 14336, 4096) == 0 and d(4, 14336, 4096) == 6 and d(16, 6144, 4096) == 6
     assert d(16, 6144, 640) == 1 and d(4, 6160, 4096) == 0
     assert d(8192, 14336, 4096) == 4 and d(8192, 14336, 6144) == 4 and d(8192, 4096, 14336) == 4 and d(8192, 14336, 256) == 4
-    assert d(512, 14336, 4096) == 3 and d(512, 4096, 4096) == 2
+    assert d(512, 14336, 4096) == 7 and d(512, 4096, 4096) == 2 and d(512, 6144, 4096) == 2
     # 256x256 tiles from 2/3 of the 128x128 configuration's rounds (256 CUs without a GPU)
-    assert d(1024, 14336, 4096) == 4 and d(2048, 4096, 4096) == 3 and d(4096, 4096, 14336) == 4
-    assert d(2048, 4096, 14336) == 3 and d(1024, 6144, 4096) == 3
+    assert d(1024, 14336, 4096) == 4 and d(4096, 4096, 14336) == 4 and d(2048, 6144, 4096) == 4
+    # one round of 256x128 tiles over 3/4 .. all of the CUs
+    assert d(2048, 4096, 4096) == 7 and d(2048, 4096, 14336) == 7 and d(1024, 6144, 4096) == 7
+    assert d(1024, 4096, 4096) == 3 and d(1024, 4096, 14336) == 3 and d(3072, 4096, 4096) == 4
     # 17..64 rows: unit decode over 16-row blocks, except above 32 rows when
     # the 64x64 tiles cover about 3/4 of the CUs
     assert d(17, 4096, 4096) == 0 and d(32, 4096, 4096) == 6 and d(64, 6144, 4096) == 6
@@ -232,9 +234,9 @@ def test_linear_algo_validation(lib):
         return f(a["xq"], a["xd"], a["xs"], a["xk"], a["m"], a["k"], a["v"], a["meta"], a["wd"], a["ws"], a["wk"],
                  a["n"], a["bias"], a["out"], a["od"], a["algo"], None)
 
-    assert call(algo=7) == DTYPE and call(algo=-2) == DTYPE
+    assert call(algo=8) == DTYPE and call(algo=-2) == DTYPE
     assert call(algo=5) == DTYPE                  # the pipelined kernel: FP8 accumulation only
-    assert call(algo=0x200) == DTYPE and call(algo=7 | F8) == DTYPE
+    assert call(algo=0x200) == DTYPE and call(algo=8 | F8) == DTYPE
     assert call(algo=0) == SHAPE                  # k = 256: not a multiple of 1024
     assert call(algo=0 | F8) == SHAPE
     assert call(algo=5 | F8) == SHAPE             # k < 512
