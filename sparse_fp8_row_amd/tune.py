@@ -21,6 +21,7 @@ rate does not set the time.
 from __future__ import annotations
 
 import json
+import time
 from typing import Iterable, Optional, Sequence, Tuple
 
 import torch
@@ -101,10 +102,12 @@ def time_algo(m: int, n: int, k: int, algo: int, x_dtype=torch.float8_e4m3fn, w_
     """Mean microseconds per call of algorithm `algo` on an (m, n, k) layer.
 
     Every weight copy is used once before timing; the timed batch holds at
-    least `reps` calls, every copy twice, and `min_ms` of GPU time, so that
-    the clocks have settled.  Up to 64 rows (kernels of a few microseconds)
-    the calls are timed inside a HIP graph, so that the host's launch rate
-    does not set the time."""
+    least `reps` calls, every copy twice, and `min_ms` of GPU time.  That
+    does not bring an idle GPU's clocks up: run the kernel for about half a
+    second first (search does) when comparing times taken in a fresh
+    process.  Up to 64 rows (kernels of a few microseconds) the calls are
+    timed inside a HIP graph, so that the host's launch rate does not set
+    the time."""
     inp = inputs if inputs is not None else _Inputs(m, n, k, x_dtype, w_dtype, rotate_bytes)
     lib = load()
     h = _stream(stream)
@@ -148,13 +151,19 @@ def time_algo(m: int, n: int, k: int, algo: int, x_dtype=torch.float8_e4m3fn, w_
 
 
 def search(shapes: Iterable[Tuple[int, int, int]], x_dtype=torch.float8_e4m3fn, w_dtype=torch.float8_e4m3fn,
-           reps: int = 20, warmup: int = 3, algos: Optional[Sequence[int]] = None) -> dict:
+           reps: int = 20, warmup: int = 3, algos: Optional[Sequence[int]] = None, settle_s: float = 0.5) -> dict:
     """Time every supported algorithm on each (m, n, k).
+
+    Before the first timing the first shape's first candidate runs for
+    `settle_s` seconds, so that a search in an idle process does not time its
+    first candidates while the clocks are still rising (which would favour
+    the later ones).
 
     Returns {"table": {(m_bucket, n, k): best algo}, "timings": [per-shape
     records with the default and best algorithm and every time in us]}."""
     names = dict(linear_algos())
     table, records = {}, []
+    settled = settle_s <= 0
     for m, n, k in shapes:
         # by default the candidates share the built-in choice's accumulation
         # (a faster but less accurate choice is never made silently)
@@ -162,6 +171,11 @@ def search(shapes: Iterable[Tuple[int, int, int]], x_dtype=torch.float8_e4m3fn, 
         pool = algos if algos is not None else [a for a in names if a & SFR_ALGO_ACC_F8 == acc]
         cand = [a for a in pool if algo_supported(a, m, n, k)]
         inp = _Inputs(m, n, k, x_dtype, w_dtype, 600 << 20)
+        if not settled and cand:
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < settle_s:
+                time_algo(m, n, k, cand[0], reps=reps, warmup=0, inputs=inp)
+            settled = True
         times = {a: time_algo(m, n, k, a, reps=reps, warmup=warmup, inputs=inp) for a in cand}
         del inp
         best = min(times, key=times.get)
