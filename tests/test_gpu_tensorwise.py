@@ -68,10 +68,11 @@ def test_tensorwise_quantize_deterministic(gpu):
     assert host_f32(outs[0][1])[0] == host_f32(outs[1][1])[0]
 
 
-# (name, m, n, k): decode, tiled, persistent 256x256 (ragged in m and n)
+# (name, m, n, k): decode, tiled, persistent 256x256 and 256x128 (ragged in m
+# and n; the last takes tiled_256x128 on a 256-CU device)
 LINEAR_SHAPES = [("decode1", 1, 4096, 4096), ("decode16", 16, 4096, 4096), ("decode_blocks", 40, 4096, 2048),
                  ("tiled", 100, 1040, 384),
-                 ("persistent", 4100, 8208, 512)]
+                 ("persistent", 4100, 8208, 512), ("persistent_256x128", 1000, 7120, 512)]
 KINDS = [("tensor", "row"), ("row", "tensor"), ("tensor", "tensor")]
 
 
