@@ -11,7 +11,9 @@ equal the oracle's and whose output must equal the FP8-input path's bit for
 bit.  The shapes reach every branch of the built-in choice (unit, register
 and 32-row decode, single-launch decode from bf16, 64x64 and 128x128 tiles,
 the persistent kernel with 256x128 and 256x256 tiles) at sizes nobody picked
-by hand.
+by hand.  A second set runs every algorithm id that supports its shape
+(each accumulation, both outputs), FP8-accumulation ids held to the bound
+plus the FP8 instruction's truncation bound, as test_gpu_algos does.
 """
 import sys
 
@@ -21,7 +23,7 @@ import torch
 
 import oracle
 import sfr_inputs
-from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, FP8_TORCH
+from parity import check_bf16, check_f32, dev_bf16, host_bf16_bits, host_bytes, host_f32, hw_bound, is_f8_acc, FP8_TORCH
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +112,53 @@ def test_random_shape(gpu, shape):
         assert np.array_equal(host_bytes(xqd), oxq)
         assert np.array_equal(host_f32(xsd).view(np.uint32), oxs.view(np.uint32))
         assert np.array_equal(host_bf16_bits(yd), host_bf16_bits(ys[torch.bfloat16]))
+
+
+def _algo_cases(count=16, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m = int(rng.integers(1, 65)) if i % 2 == 0 else int(rng.integers(65, 1201))
+        k = 1024 * int(rng.integers(1, 4)) if i % 4 < 2 else 128 * int(rng.integers(1, 25))
+        n = 32 * int(rng.integers(1, 129))   # a multiple of 32: the 32-row decode can run
+        xf, wf = [(E4, E4), (E4, E5), (E5, E4), (E5, E5)][int(rng.integers(0, 4))]
+        out.append((m, n, k, xf, wf, bool(rng.random() < 0.5)))
+    return out
+
+
+ALGO_CASES = _algo_cases()
+
+
+@pytest.mark.parametrize("shape", ALGO_CASES, ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}")
+def test_random_shape_every_algo(gpu, shape):
+    m, n, k, xf, wf, bias = shape
+    case = sfr_inputs.Case("random_algo", 18, m, n, k, x_fmt=xf, w_fmt=wf, bias=bias)
+    xb, wb, bb = sfr_inputs.draw_x(case), sfr_inputs.draw_w(case), sfr_inputs.draw_bias(case)
+    rows = np.arange(m)
+    if m > SAMPLED_ROWS:
+        rng = np.random.default_rng(m * 37 + n + k)
+        rows = np.unique(np.concatenate([rng.choice(m, SAMPLED_ROWS, replace=False), [0, m - 1]]))
+    oxq, oxs = oracle.quantize_rows(xb, xf)
+    ov, om, ows, _ = oracle.prepare_weight(wb, wf)
+    ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows, bias=bb, rows=rows)
+    hwb = hw_bound(oxq, xf, oxs, oracle.decompress_2to4(ov, om), wf, ows, rows, np.arange(n))
+    xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(xb), FP8_TORCH[xf])
+    pw = gpu.prepare_weight(dev_bf16(wb), FP8_TORCH[wf])
+    b = None if bb is None else dev_bf16(bb)
+    ran = 0
+    for algo, aname in gpu.linear_algos():
+        if not gpu.algo_supported(algo, m, n, k):
+            continue
+        for od in (torch.bfloat16, torch.float32):
+            say(f"random algo {aname} {case.name} out={od}")
+            y = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, b, out_dtype=od, algo=algo)
+            torch.cuda.synchronize()
+            allow = hwb if is_f8_acc(algo) else None
+            if od == torch.float32:
+                r = check_f32(host_f32(y)[rows], ref, bb is not None, allow)
+            else:
+                r = check_bf16(host_bf16_bits(y)[rows], ref, allow)
+            say(f"  {r}")
+            assert r["bad"] == 0, r
+        ran += 1
+    assert ran >= 6   # the tiled configurations (three sizes, 256x128) with both accumulations at least
