@@ -9,7 +9,8 @@ and the Llama-3.1-8B shapes at sparsity 0.9.  Linear (bsr_linear_bf16):
 binary32 output within 1e-5 * sum |x * w| (+ the bias add's half ulp) of the
 binary64 oracle, bf16 output within one bf16 ulp of the oracle's rounding of
 it (or inside that tolerance window), for M = 1 .. 40 (ragged 16-row tiles),
-with and without bias, many kept blocks per row and empty block rows."""
+with and without bias, many kept blocks per row and empty block rows, and on
+12 seeded random shapes (M up to 80, N and K up to 8192, sparsity 0 .. 0.97)."""
 import sys
 
 import numpy as np
@@ -109,3 +110,22 @@ def test_bsr_linear_deterministic(gpu):
         y1 = gpu.bsr_linear(x, bw, b, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+
+
+def _random_linear(count=12, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        m = int(rng.integers(1, 81))
+        n, k = 64 * int(rng.integers(1, 129)), 64 * int(rng.integers(1, 129))
+        sparsity = float(rng.choice([0.0, 0.5, 0.9, 0.97, float(rng.random())]))
+        out.append((m, n, k, sparsity, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_linear(), ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}s{s[3]:.2f}")
+def test_bsr_linear_random_shapes(gpu, shape):
+    # seeded random shapes: M 1 .. 80 (up to five 16-row tiles, ragged),
+    # N and K multiples of 64 up to 8192, sparsity from dense to 0.97
+    m, n, k, sparsity, bias = shape
+    run_linear(gpu, sfr_inputs.Case("bsr_rand", 23, m, n, k, bias=bias), sparsity, bias)

@@ -68,6 +68,25 @@ def test_tensorwise_quantize_deterministic(gpu):
     assert host_f32(outs[0][1])[0] == host_f32(outs[1][1])[0]
 
 
+def _random_tensors(count=10, seed=20261206):
+    rng = np.random.default_rng(seed)
+    kinds = ["normal", "student", "wide", "tiny", "edge"]
+    return [(int(rng.integers(1, 301)), 8 * int(rng.integers(1, 3001)), kinds[int(rng.integers(0, 5))],
+             [E4, E5][int(rng.integers(0, 2))]) for _ in range(count)]
+
+
+@pytest.mark.parametrize("rows,cols,kind,fmt", _random_tensors(), ids=lambda v: str(v))
+def test_tensorwise_quantize_random_shapes(gpu, rows, cols, kind, fmt):
+    # seeded random tensors (rows 1 .. 300, cols a multiple of 8 up to 24000)
+    x = rows_bits(kind, rows, cols, rows * 11 + cols)
+    say(f"quantize_tensorwise random {kind} ({rows}, {cols}) fmt={fmt}")
+    q, s = gpu.quantize_tensorwise_fp8(dev_bf16(x), FP8_TORCH[fmt])
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quantize_tensor(x, fmt)
+    assert host_f32(s).view(np.uint32)[0] == os_.view(np.uint32)[0]
+    assert np.array_equal(host_bytes(q), oq)
+
+
 # (name, m, n, k): decode, tiled, persistent 256x256 and 256x128 (ragged in m
 # and n; the last takes tiled_256x128 on a 256-CU device)
 LINEAR_SHAPES = [("decode1", 1, 4096, 4096), ("decode16", 16, 4096, 4096), ("decode_blocks", 40, 4096, 2048),
