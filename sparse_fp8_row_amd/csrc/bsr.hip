@@ -239,8 +239,8 @@ __global__ __launch_bounds__(64 * NW) void bsr_linear_kernel(const uint16_t* __r
     if (m < M) {
       if constexpr (OUT == OUT_BF16) {
         uint16_t* o = reinterpret_cast<uint16_t*>(out) + (int64_t)m * N + n;
-        const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        const uint32_t lo = pack_bf16x2(y[0], y[1]);
+        const uint32_t hi = pack_bf16x2(y[2], y[3]);
         *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
       } else {
         *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + (int64_t)m * N + n) = y;

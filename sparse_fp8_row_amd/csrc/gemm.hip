@@ -70,8 +70,8 @@ template <int OUT>
 __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t n, v4f y) {
   if constexpr (OUT == OUT_BF16) {
     uint16_t* o = reinterpret_cast<uint16_t*>(out) + m * ld + n;
-    const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-    const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+    const uint32_t lo = pack_bf16x2(y[0], y[1]);
+    const uint32_t hi = pack_bf16x2(y[2], y[3]);
     *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
   } else {
     float* o = reinterpret_cast<float*>(out) + m * ld + n;
@@ -177,8 +177,8 @@ __device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[FN][FM], co
         y[2] += bf16_to_f32(bv[fn].y & 0xFFFFu);
         y[3] += bf16_to_f32(bv[fn].y >> 16);
       }
-      const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-      const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+      const uint32_t lo = pack_bf16x2(y[0], y[1]);
+      const uint32_t hi = pack_bf16x2(y[2], y[3]);
       // outputs n = 16 fn + 4 lg .. + 3: chunk 2 fn + lg / 2, half lg % 2
       const int c = (2 * fn + (lg >> 1)) ^ (row & (CPR - 1));
       *reinterpret_cast<uint2*>(region + row * (CPR * 16) + c * 16 + 8 * (lg & 1)) = make_uint2(lo, hi);
@@ -837,8 +837,8 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void linear_persistent_kernel(
             y[2] += bf16_to_f32(bv[fn].y & 0xFFFFu);
             y[3] += bf16_to_f32(bv[fn].y >> 16);
           }
-          const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+          const uint32_t lo = pack_bf16x2(y[0], y[1]);
+          const uint32_t hi = pack_bf16x2(y[2], y[3]);
           const int c = (2 * fn + (lg >> 1)) ^ (row & 7);
           *reinterpret_cast<uint2*>(reg + row * 128 + c * 16 + 8 * (lg & 1)) = make_uint2(lo, hi);
         }
@@ -1236,8 +1236,8 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 constexpr int kUnitK = 1024;
 constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
 enum { XM_DIRECT = 0, XM_ONE_ROW = 1, XM_PERMUTED = 2 };
-template <int XF, int WF, int OUT, int ACC, int RT, int XM>
-__global__ __launch_bounds__(512, RT == 1 ? 4 : 2) void linear_decode_unit_kernel(
+template <int XF, int WF, int OUT, int ACC, int RT, int XM, int MAXW = 8>
+__global__ __launch_bounds__(64 * MAXW, RT == 1 ? 4 : 2) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
     const uint8_t* __restrict__ meta, const float* __restrict__ ws, const uint16_t* __restrict__ bias,
     void* __restrict__ out, int M, int N, int K, int xs_stride, int ws_stride) {
@@ -1465,20 +1465,36 @@ hipError_t run_persistent(const LinearArgs& a, hipStream_t stream) {
 
 // Wavefronts per workgroup of the unit decode kernel: the K / 1024 units
 // spread evenly over at most 8 wavefronts.
-inline int unit_waves(int64_t k) {
-  const int nu = (int)(k / kUnitK), per = (nu + 7) / 8;
+inline int unit_waves(int64_t k, int maxw = 8) {
+  const int nu = (int)(k / kUnitK), per = (nu + maxw - 1) / maxw;
   return (nu + per - 1) / per;
 }
 
-template <int XF, int WF, int OUT, int ACC, int RT, int XM>
-hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
-  auto kern = linear_decode_unit_kernel<XF, WF, OUT, ACC, RT, XM>;
-  const int nw = unit_waves(a.k);
+// Wavefronts per workgroup of the unit kernel: at most 8, so that several
+// workgroups share a CU.  Up to 16 (one unit per wavefront up to K = 16384,
+// 160 KB of LDS at most) for the binary32-grade step with 16 weight rows and
+// 2..16 activation rows per workgroup, more than 8 units of K and workgroups
+// that all fit on the CUs at once: the widening work after each wavefront's
+// wait is then spread over twice the wavefronts instead of following a
+// second unit's wait.  Measured on the down projection (N = 4096,
+// K = 14336): M = 16 12.41 -> 11.75 us, M = 4 10.75 -> 10.68 us; one row
+// (the broadcast form, little work per unit) 9.23 -> 9.46 us, and FP8
+// accumulation (no widening) 11.92 -> 12.02 us at M = 16, so those keep 8.
+template <int RT, int ACC, int XM>
+inline int unit_max_waves(const LinearArgs& a) {
+  if (RT != 1 || ACC != ACC_F32 || XM == XM_ONE_ROW || a.k <= 8 * kUnitK) return 8;
+  return (a.n / 16) * ((a.m + 15) / 16) <= device_cus() ? 16 : 8;
+}
+
+template <int XF, int WF, int OUT, int ACC, int RT, int XM, int MAXW>
+hipError_t run_decode_unit_waves(const LinearArgs& a, hipStream_t stream) {
+  auto kern = linear_decode_unit_kernel<XF, WF, OUT, ACC, RT, XM, MAXW>;
+  const int nw = unit_waves(a.k, MAXW);
   const unsigned lds = (unsigned)(nw * RT * kUnitLds);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 8 * RT * kUnitLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, MAXW * RT * kUnitLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1486,6 +1502,14 @@ hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
                      a.xq, a.xs, a.values,
                      a.meta, a.ws, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, a.xs_stride, a.ws_stride);
   return hipGetLastError();
+}
+
+template <int XF, int WF, int OUT, int ACC, int RT, int XM>
+hipError_t run_decode_unit_cfg(const LinearArgs& a, hipStream_t stream) {
+  if constexpr (RT == 1 && ACC == ACC_F32 && XM != XM_ONE_ROW) {
+    if (unit_max_waves<RT, ACC, XM>(a) == 16) return run_decode_unit_waves<XF, WF, OUT, ACC, RT, XM, 16>(a, stream);
+  }
+  return run_decode_unit_waves<XF, WF, OUT, ACC, RT, XM, 8>(a, stream);
 }
 
 template <int XF, int WF, int OUT, int ACC, int RT>

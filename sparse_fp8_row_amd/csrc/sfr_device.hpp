@@ -29,14 +29,16 @@ __device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
   else return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
 }
 
-// binary32 -> bf16 bits, round to nearest even (finite inputs; overflow gives inf).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Two binary32 values -> two bf16 rounded to nearest even, a in the low half,
+// in one instruction (V_CVT_PK_BF16_F32; subnormals kept, as the kernels run
+// with binary32 denormals on; overflow gives inf, NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
+}
 
 // 2:4 sparse x dense FP8 MFMA, 16x16 output, 128 dense k per instruction.
 // A (sparse weight, format WF): lane l holds row l%16, kept values of dense

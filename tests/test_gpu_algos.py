@@ -107,3 +107,37 @@ def test_search_and_table(gpu):
     y2 = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, pw.scale, algo=best)
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(y1), host_bf16_bits(y2))
+
+
+def test_subnormal_outputs(gpu):
+    """bf16 rounding of outputs in the binary32 / bf16 subnormal range, in
+    every kernel's epilogue: scales 2^-60 (rows) and 2^-84 (outputs) make
+    xs * ws = 2^-144 exactly, so most outputs land below 2^-126; each must be
+    within one bf16 ulp of the oracle's value (a converter that flushed
+    subnormals would give zeros)."""
+    m, n, k, xf, wf = 48, 256, 1024, E4, E4
+    case = sfr_inputs.Case("algo_subnormal", 15, m, n, k, x_fmt=xf, w_fmt=wf)
+    xb, wb = sfr_inputs.draw_x(case), sfr_inputs.draw_w(case)
+    oxq, _ = oracle.quantize_rows(xb, xf)
+    ov, om, _, _ = oracle.prepare_weight(wb, wf)
+    oxs = np.full(m, 2.0**-60, np.float32)
+    ows = np.full(n, 2.0**-84, np.float32)
+    ref = oracle.linear(oxq, xf, oxs, ov, om, wf, ows)
+    sub = (np.abs(ref["y"]) < 2.0**-126) & (np.abs(ref["y"]) >= 2.0**-133)
+    assert sub.mean() > 0.3, f"only {sub.mean():.2f} of the outputs are subnormal"
+    xq, xs = gpu.quantize_rowwise_fp8(dev_bf16(xb), FP8_TORCH[xf])
+    pw = gpu.prepare_weight(dev_bf16(wb), FP8_TORCH[wf])
+    xs = torch.full_like(xs, 2.0**-60)
+    ws = torch.full_like(pw.scale, 2.0**-84)
+    ran = 0
+    for algo, aname in gpu.linear_algos():
+        if is_f8_acc(algo) or not gpu.algo_supported(algo, m, n, k):
+            continue
+        say(f"subnormal outputs: {aname}")
+        y = gpu.sparse_fp8_scaled_linear(xq, xs, pw.values, pw.meta, ws, algo=algo)
+        torch.cuda.synchronize()
+        r = check_bf16(host_bf16_bits(y), ref)
+        say(f"  {r}")
+        assert r["bad"] == 0, (aname, r)
+        ran += 1
+    assert ran >= 5
