@@ -35,7 +35,11 @@ SHAPES = [("all_algos", 7, 1040, 1024, E4, E4, True), ("tiled", 300, 4112, 640, 
           ("deep_pipeline", 200, 1040, 8320, E5, E4, True),
           # the unit decode kernels over 16-row activation blocks: 4 blocks,
           # the last with 2 rows
-          ("decode_column_blocks", 50, 1056, 2048, E4, E5, True)]
+          ("decode_column_blocks", 50, 1056, 2048, E4, E5, True),
+          # more than 8 units with workgroups that fit the CUs at once: one
+          # unit per wavefront on up to 16 wavefronts (9 here, and 14 with the
+          # down projection's K at 3 rows)
+          ("decode_waves_9", 7, 1040, 9216, E5, E4, True), ("decode_waves_14", 3, 4096, 14336, E4, E4, False)]
 
 
 @pytest.fixture(scope="module", autouse=True)
