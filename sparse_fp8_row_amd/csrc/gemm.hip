@@ -1218,13 +1218,14 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 // rows and K / 1024 "units" of 1024 k (8 MFMA steps) each; wavefront w takes
 // units w, w + NW, ...  For a unit it puts the unit's compressed values
 // (512 contiguous bytes per row) and metadata (128 bytes per row) in flight
-// into its own RT * 10 KB of LDS with 1 KB global_load_lds instructions, and
-// the activation operands of the unit's 8 steps straight into registers
-// (shared by the RT row tiles), then waits for its own loads only and runs
-// the 8 * RT MFMAs: no workgroup barrier before the final fixed-order
-// reduction, so every wavefront computes as soon as its data is there while
-// the others' loads stream.  LDS holds only the weight block, so several
-// workgroups share a CU.  Each 16-byte chunk of a row is stored at
+// into its own RT * 10 KB of LDS with 1 KB buffer->LDS loads, in two halves
+// of 4 steps (unit_two_halves), and the activation operands of the unit's 8
+// steps straight into registers (shared by the RT row tiles); it waits for
+// the first half of its own loads only and runs those 4 * RT MFMAs while the
+// second half lands, then the rest: no workgroup barrier before the final
+// fixed-order reduction, so every wavefront computes as soon as its data is
+// there while the others' loads stream.  LDS holds only the weight block, so
+// several workgroups share a CU.  Each 16-byte chunk of a row is stored at
 // chunk ^ (row & 7) (a permutation inside 128-byte groups, applied to the
 // source addresses of each 1 KB load), which makes the MFMA-layout LDS reads
 // conflict-free.  RT = 2 halves the activation traffic (every workgroup reads
@@ -1236,6 +1237,170 @@ __device__ __forceinline__ void x1_unit(v4f& acc0, v4f& acc1, const v4i& x1, con
 constexpr int kUnitK = 1024;
 constexpr int kUnitLds = 16 * kUnitK / 2 + 16 * kUnitK / 8;  // 10 KB per 16 rows
 enum { XM_DIRECT = 0, XM_ONE_ROW = 1, XM_PERMUTED = 2 };
+constexpr int kHalfLds = kUnitLds / 2;  // one half unit (4 steps) of 16 rows: 4 KB values + 1 KB metadata
+
+// Offsets of the unit kernel's two-half layout.  Half h of a unit (its steps
+// 4h .. 4h + 3) of row tile t sits at (h * RT + t) * kHalfLds of the
+// wavefront's region: 16 rows x 256 bytes of values, then 16 rows x 64 bytes
+// of metadata.  Values load i (0..3) of a half brings rows 4i .. 4i + 3, lane
+// L the row's 16-byte chunk (L % 16) ^ (row & 7) (row & 7 = 4 (i & 1) + L / 16)
+// to 16 L; the metadata load brings row L / 4, step (L % 4) ^ (row & 3) of the
+// half.  Reads of step s (s4 = s % 4): lane (r16, lg) finds values chunk
+// 4 s4 + lg of row r16 at chunk (4 s4 + lg) ^ (r16 & 7) and the metadata of
+// step s4 at chunk s4 ^ (r16 & 3), which keeps the 128-bit reads of 8
+// consecutive rows on distinct banks.
+struct UnitHalfOffsets {
+  uint32_t voff[2], moff, a_even, a_odd, i_row;
+  int r3;
+  __device__ UnitHalfOffsets(int lane, int K) {
+    const int r16 = lane & 15, lg = lane >> 4, r7 = r16 & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      voff[p] = (uint32_t)((lane >> 4) * (K / 2) + 16 * ((lane & 15) ^ (4 * p + (lane >> 4))));
+    moff = (uint32_t)((lane >> 2) * (K / 8) + 16 * ((lane & 3) ^ ((lane >> 2) & 3)));
+    a_even = r16 * 256 + 16 * ((4 * ((r7 >> 2) & 1)) | (lg ^ (r7 & 3)));
+    a_odd = r16 * 256 + 16 * ((4 * (((r7 >> 2) & 1) ^ 1)) | (lg ^ (r7 & 3)));
+    i_row = 4096 + r16 * 64 + 4 * lg;
+    r3 = r16 & 3;
+  }
+};
+
+// Global -> LDS loads of half h of unit u0 for RT row tiles into hb, through
+// buffer descriptors of the workgroup's weight rows (rv: values, rm:
+// metadata): the lane offsets stay in fixed registers and everything else is
+// a scalar offset.
+template <int RT>
+__device__ __forceinline__ void unit_half_loads(uint8_t* __restrict__ hb, __amdgpu_buffer_rsrc_t rv,
+                                                __amdgpu_buffer_rsrc_t rm, const UnitHalfOffsets& o, int u0, int h,
+                                                int K) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    uint8_t* dst = hb + t * kHalfLds;
+    const int sv = 16 * t * (K / 2) + u0 * (kUnitK / 2) + 256 * h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buffer_lds16(rv, dst + i * 1024, (int)o.voff[i & 1], sv + 4 * i * (K / 2));
+    buffer_lds16(rm, dst + 4096, (int)o.moff, 16 * t * (K / 8) + u0 * (kUnitK / 8) + 64 * h);
+  }
+}
+
+// b[d] = the value b[d] of lane xsrc / 4, for the 8 words of one step's
+// activation (ds_bpermute), with the wait for the results in the same block.
+// Written as assembly because the compiler treats its own lane permutation as
+// an LDS access and would make it wait for every global->LDS load in flight,
+// including those of the unit's second half; the permutation neither reads
+// nor writes LDS memory.
+__device__ __forceinline__ void bpermute8(v8i& b, int xsrc) {
+  int r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_bpermute_b32 %0, %8, %9\n\t"
+      "ds_bpermute_b32 %1, %8, %10\n\t"
+      "ds_bpermute_b32 %2, %8, %11\n\t"
+      "ds_bpermute_b32 %3, %8, %12\n\t"
+      "ds_bpermute_b32 %4, %8, %13\n\t"
+      "ds_bpermute_b32 %5, %8, %14\n\t"
+      "ds_bpermute_b32 %6, %8, %15\n\t"
+      "ds_bpermute_b32 %7, %8, %16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(xsrc), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+  b = v8i{r0, r1, r2, r3, r4, r5, r6, r7};
+}
+
+// Steps S0 .. S0 + 3 of a unit from half hb (RT row tiles), activation b.
+template <int XF, int WF, int ACC, int RT, int XM, int S0>
+__device__ __forceinline__ void unit_half_steps(const uint8_t* __restrict__ hb, v8i (&b)[8], v4f (&acc0)[RT],
+                                                v4f (&acc1)[RT], const UnitHalfOffsets& o, int xsrc) {
+#pragma unroll
+  for (int s = S0; s < S0 + 4; ++s) {
+    const int s4 = s & 3;
+    if constexpr (XM == XM_PERMUTED) bpermute8(b[s], xsrc);
+    if constexpr (ACC == ACC_F32) {
+      // the activation half widened once for the RT row tiles
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const v8i bw = hh ? widen_b_half<XF, 1>(b[s]) : widen_b_half<XF, 0>(b[s]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const uint8_t* rt = hb + t * kHalfLds;
+          const v4i a = *reinterpret_cast<const v4i*>(rt + ((s4 & 1) ? o.a_odd : o.a_even) + 128 * (s4 >> 1));
+          const int idx = *reinterpret_cast<const int*>(rt + o.i_row + 16 * (s4 ^ o.r3));
+          const v4i aw = hh ? widen_a_half<WF, 1>(a) : widen_a_half<WF, 0>(a);
+          const int ix = hh ? idx_half<1>(idx) : idx_half<0>(idx);
+          if (s & 1) acc1[t] = smfmac16_bf16(aw, bw, acc1[t], ix);
+          else acc0[t] = smfmac16_bf16(aw, bw, acc0[t], ix);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint8_t* rt = hb + t * kHalfLds;
+        const v4i a = *reinterpret_cast<const v4i*>(rt + ((s4 & 1) ? o.a_odd : o.a_even) + 128 * (s4 >> 1));
+        const int idx = *reinterpret_cast<const int*>(rt + o.i_row + 16 * (s4 ^ o.r3));
+        if (s & 1) acc1[t] = smfmac16<XF, WF>(a, b[s], acc1[t], idx);
+        else acc0[t] = smfmac16<XF, WF>(a, b[s], acc0[t], idx);
+      }
+    }
+  }
+}
+
+// One unit of the unit kernel in two halves: the loads of half 0 (and the
+// activation of its steps) go out before those of half 1, so the wavefront
+// computes steps 0-3 while the rest of its block is still in flight
+// (measured against one wait for the whole unit: 0.45-0.87 us faster at
+// M = 4 and 16 on the Llama shapes, the same at M = 1).  h0 and h1 are
+// restrict parameters of an inlined function, so the compiler can tell the
+// reads of half 0 from the pending loads of half 1 and waits for half 0
+// alone.
+template <int XF, int WF, int ACC, int RT, int XM>
+__device__ __forceinline__ void unit_two_halves(uint8_t* __restrict__ h0, uint8_t* __restrict__ h1,
+                                                __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rm,
+                                                const uint8_t* __restrict__ xq, const uint8_t* xrow,
+                                                const UnitHalfOffsets& o, int u0, int K, int r16, int lg, int xsrc,
+                                                v4f (&acc0)[RT], v4f (&acc1)[RT]) {
+  v8i b[8];
+  v4i x1;
+  if constexpr (XM == XM_ONE_ROW) {
+    // one activation row: lane (r16, lg) holds chunk 8 (r16 >> 1) + 4 (r16 & 1) + lg
+    // of the unit, i.e. the half r16 & 1 of step r16 >> 1 that lane group lg needs
+    x1 = *reinterpret_cast<const v4i*>(xq + u0 * kUnitK + 128 * (r16 >> 1) + 64 * (r16 & 1) + 16 * lg);
+    // the memory clobbers keep the issue order the counts below assume
+    asm volatile("" ::: "memory");
+    unit_half_loads<RT>(h0, rv, rm, o, u0, 0, K);
+    asm volatile("" ::: "memory");
+    unit_half_loads<RT>(h1, rv, rm, o, u0, 1, K);
+    asm volatile("" ::: "memory");
+    wait_vmcnt<5 * RT>();  // x1 and half 0 have landed
+    __builtin_amdgcn_sched_barrier(0);
+    // step s's operand: lanes 2s and 2s + 1 of each 16-lane row, broadcast
+    // to the whole row (DPP row_newbcast)
+    row_bcast_steps(b, x1, std::make_integer_sequence<int, 8>{});
+  } else {
+    const uint8_t* xp = xrow + u0 * kUnitK;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int s = 4 * hf; s < 4 * hf + 4; ++s) {
+        const v4i l = *reinterpret_cast<const v4i*>(xp + s * 128);
+        const v4i h = *reinterpret_cast<const v4i*>(xp + s * 128 + 64);
+        b[s] = __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      // the memory clobbers keep the issue order the counts below assume
+      asm volatile("" ::: "memory");
+      unit_half_loads<RT>(hf ? h1 : h0, rv, rm, o, u0, hf, K);
+      asm volatile("" ::: "memory");
+    }
+    // nothing that uses the loaded operands (the lane permutations included)
+    // moves above this point
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<8 + 5 * RT>();  // the activation of steps 0-3 and half 0 have landed
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  unit_half_steps<XF, WF, ACC, RT, XM, 0>(h0, b, acc0, acc1, o, xsrc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  unit_half_steps<XF, WF, ACC, RT, XM, 4>(h1, b, acc0, acc1, o, xsrc);
+}
 template <int XF, int WF, int OUT, int ACC, int RT, int XM, int MAXW = 8>
 __global__ __launch_bounds__(64 * MAXW, RT == 1 ? 4 : 2) void linear_decode_unit_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ values,
@@ -1248,15 +1413,7 @@ __global__ __launch_bounds__(64 * MAXW, RT == 1 ? 4 : 2) void linear_decode_unit
   const int r16 = lane & 15, lg = lane >> 4;
   const int NU = K / kUnitK;
   uint8_t* region = smem + wave * (RT * kUnitLds);
-  // DMA lane roles: values load i covers rows 2i, 2i + 1 of a row tile (32
-  // chunks each), at a uniform offset i * K plus a lane offset that repeats
-  // with period 4 in i (the swizzle depends on row & 7); metadata load i covers
-  // rows 8i .. 8i + 7 (8 chunks each), uniform offset i * K plus one lane offset
-  const int vrow_l = lane >> 5, vc = lane & 31, mrow_l = lane >> 3, mc = lane & 7;
-  uint32_t voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(vrow_l * (K / 2) + 16 * (vc ^ ((2 * i + vrow_l) & 7)));
-  const uint32_t moff = (uint32_t)(mrow_l * (K / 8) + 16 * (mc ^ (mrow_l & 7)));
+  const UnitHalfOffsets o(lane, K);
   // workgroup row blockIdx.y takes activation rows mb .. mb + 15 (M up to
   // 64: the weight block is read once per 16 rows, mostly from L2).  Rows
   // past the last, Mc, read row Mc - 1: MFMA output column m depends on
@@ -1275,12 +1432,6 @@ __global__ __launch_bounds__(64 * MAXW, RT == 1 ? 4 : 2) void linear_decode_unit
       XM == XM_PERMUTED ? xq + (int64_t)(mb + min(lane >> 2, Mc - 1)) * K + 16 * (lane & 3)
                         : xq + (int64_t)(mb + min(r16, Mc - 1)) * K + 16 * lg;
   const int xsrc = 4 * (4 * r16 + lg);  // byte address of the source lane of (r16, lg)
-  // LDS read offsets: step s's values chunk 4s + lg of row r16 sits at chunk
-  // (4s + lg) ^ (r16 & 7) = 8 (s >> 1) + ab[s & 1]; its metadata chunk at s ^ (r16 & 7)
-  const int r7 = r16 & 7;
-  const uint32_t a_even = r16 * 512 + 16 * ((4 * ((r7 >> 2) & 1)) | (lg ^ (r7 & 3)));
-  const uint32_t a_odd = r16 * 512 + 16 * ((4 * (((r7 >> 2) & 1) ^ 1)) | (lg ^ (r7 & 3)));
-  const uint32_t i_row = 8192 + r16 * 128 + 4 * lg;
 
   const int m = r16;
   float xsm = 0.f;
@@ -1299,74 +1450,13 @@ __global__ __launch_bounds__(64 * MAXW, RT == 1 ? 4 : 2) void linear_decode_unit
   v4f acc0[RT], acc1[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc0[t] = acc1[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the workgroup's RT * 16 weight rows (N is a multiple of 16 RT)
+  const int64_t n0 = (int64_t)blockIdx.x * RT * 16;
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(values + n0 * (K / 2), RT * 16 * (K / 2));
+  const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(meta + n0 * (K / 8), RT * 16 * (K / 8));
   for (int u0 = wave; u0 < NU; u0 += NW) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int64_t n0 = (int64_t)(blockIdx.x * RT + t) * 16;
-      const uint8_t* vu = values + n0 * (K / 2) + u0 * (kUnitK / 2);
-      const uint8_t* mu = meta + n0 * (K / 8) + u0 * (kUnitK / 8);
-      uint8_t* rt = region + t * kUnitLds;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(vu + (int64_t)i * K + voff[i & 3]), (void*)(rt + i * 1024), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(mu + (int64_t)i * K + moff), (void*)(rt + 8192 + i * 1024), 16, 0, 0);
-    }
-    v8i b[8];
-    v4i x1;
-    if constexpr (XM == XM_ONE_ROW) {
-      // one activation row: lane (r16, lg) holds chunk 8 (r16 >> 1) + 4 (r16 & 1) + lg
-      // of the unit, i.e. the half r16 & 1 of step r16 >> 1 that lane group lg needs
-      x1 = *reinterpret_cast<const v4i*>(xq + u0 * kUnitK + 128 * (r16 >> 1) + 64 * (r16 & 1) + 16 * lg);
-    } else {
-      const uint8_t* xp = xrow + u0 * kUnitK;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const v4i l = *reinterpret_cast<const v4i*>(xp + s * 128);
-        const v4i h = *reinterpret_cast<const v4i*>(xp + s * 128 + 64);
-        b[s] = __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
-    wait_vmcnt<0>();
-    if constexpr (XM == XM_ONE_ROW) {
-      // step s's operand: lanes 2s and 2s + 1 of each 16-lane row, broadcast
-      // to the whole row (DPP row_newbcast)
-      row_bcast_steps(b, x1, std::make_integer_sequence<int, 8>{});
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if constexpr (XM == XM_PERMUTED) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) b[s][d] = __builtin_amdgcn_ds_bpermute(xsrc, b[s][d]);
-      }
-      if constexpr (ACC == ACC_F32) {
-        // the activation half widened once for the RT row tiles
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const v8i bw = hh ? widen_b_half<XF, 1>(b[s]) : widen_b_half<XF, 0>(b[s]);
-#pragma unroll
-          for (int t = 0; t < RT; ++t) {
-            const uint8_t* rt = region + t * kUnitLds;
-            const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
-            const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
-            const v4i aw = hh ? widen_a_half<WF, 1>(a) : widen_a_half<WF, 0>(a);
-            const int ix = hh ? idx_half<1>(idx) : idx_half<0>(idx);
-            if (s & 1) acc1[t] = smfmac16_bf16(aw, bw, acc1[t], ix);
-            else acc0[t] = smfmac16_bf16(aw, bw, acc0[t], ix);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const uint8_t* rt = region + t * kUnitLds;
-          const v4i a = *reinterpret_cast<const v4i*>(rt + ((s & 1) ? a_odd : a_even) + 128 * (s >> 1));
-          const int idx = *reinterpret_cast<const int*>(rt + i_row + 16 * (s ^ r7));
-          if (s & 1) acc1[t] = smfmac16<XF, WF>(a, b[s], acc1[t], idx);
-          else acc0[t] = smfmac16<XF, WF>(a, b[s], acc0[t], idx);
-        }
-      }
-    }
+    unit_two_halves<XF, WF, ACC, RT, XM>(region, region + RT * kHalfLds, rv, rm, xq, xrow, o, u0, K, r16, lg, xsrc,
+                                         acc0, acc1);
     // the region's reads are complete (their values fed the MFMAs) before
     // the next unit's loads overwrite it
     __builtin_amdgcn_s_waitcnt(0xC07F);
