@@ -1874,15 +1874,16 @@ __global__ __launch_bounds__(64 * NWMAX, NWMAX <= 4 ? 4 : 2) void linear_decode_
 //  - 1 or 2 rows, K a multiple of 1024: up to 4096 always; up to 16384 while
 //    the workgroups (16 weight rows each) fit the CUs once (at N = 6144,
 //    K = 8192 two launches were 1.6 .. 2.8 us faster);
-//  - 3 or 4 rows: K up to 4096 and at most 1.5 workgroups per CU (at 4096
-//    one launch is 0.7 us faster, at 6144 even, at 14336 and at K = 8192 two
-//    launches are faster).
+//  - 3 or 4 rows: K up to 4096 and workgroups that fit the CUs once (at
+//    N = 4096 one launch is 0.15 us faster; at 6144, 14336 and K = 8192 two
+//    launches are faster: 8.67 against 9.35 us at N = 6144 since the unit
+//    kernel computes the first half of each unit while the second lands).
 inline int fused_rows(int64_t m) { return m == 1 ? 1 : m == 2 ? 2 : 4; }
 inline bool fused_decode_ok(int64_t m, int64_t n, int64_t k) {
   if (m < 1 || m > 4 || k % kUnitK != 0) return false;
   const int64_t wgs = n / 16, cus = device_cus();
   if (m <= 2) return k <= 4 * kUnitK || (k <= 16 * kUnitK && wgs <= cus);
-  return k <= 4 * kUnitK && 2 * wgs <= 3 * cus;
+  return k <= 4 * kUnitK && wgs <= cus;
 }
 
 template <int XF, int WF, int OUT, int ACC, int NWMAX, int MR>

@@ -67,12 +67,12 @@ def run_case(gpu, case, wscale="row", seed_shift=0):
 
 
 # (m, n, k): fused shapes (n/16 workgroups: 16 .. 896, more than the chip's 256 CUs
-# at K <= 4096; K/1024 units over up to 8 wavefronts: 1, 2, 3, 4, 5 x (2,2,2,2,1),
-# 7 x 2, 8 x 2)
+# at K <= 4096 with 1 or 2 rows, up to 256 with 3 or 4; K/1024 units over up to
+# 8 wavefronts: 1, 2, 3, 4, 5 x (2,2,2,2,1), 7 x 2, 8 x 2)
 FUSED = [(1, 4096, 4096), (1, 1040, 1024), (1, 14336, 4096), (1, 256, 2048), (1, 2048, 9216), (1, 512, 14336),
          (1, 4096, 16384), (2, 4096, 4096), (2, 1040, 1024), (2, 512, 14336), (2, 1024, 16384), (2, 4096, 9216),
-         (2, 14336, 4096), (3, 1024, 2048), (3, 256, 3072), (3, 6144, 4096), (4, 4096, 4096), (4, 1040, 1024),
-         (4, 6144, 3072), (4, 512, 3072)]
+         (2, 14336, 4096), (3, 1024, 2048), (3, 256, 3072), (3, 4096, 4096), (4, 4096, 4096), (4, 1040, 1024),
+         (4, 3072, 3072), (4, 512, 3072)]
 
 
 @pytest.mark.parametrize("shape", FUSED, ids=lambda s: f"M{s[0]}N{s[1]}K{s[2]}")
@@ -132,8 +132,8 @@ def test_dynamic_zero_rows_multi(gpu, m, zero_rows):
 # shapes that take the two-launch path: m > 4 (16 or 32 weight rows per
 # workgroup in the linear layer), k not a multiple of 1024, k above 16384
 # (above 4096 with 3 or 4 rows), k above 4096 with more workgroups than CUs,
-# 3 or 4 rows over more than 1.5 workgroups per CU
-@pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 6144, 16384), (1, 4096, 640),
+# 3 or 4 rows over more workgroups than CUs
+@pytest.mark.parametrize("shape", [(17, 1024, 1024), (5, 512, 640), (16, 6144, 16384), (1, 4096, 640), (4, 6144, 3072),
                                    (1, 256, 17408), (3, 1024, 640), (2, 4096, 17408), (4, 4096, 9216),
                                    (16, 4096, 4096), (3, 1024, 14336), (7, 4096, 14336), (16, 4096, 14336),
                                    (16, 14336, 4096), (8, 6144, 4096), (13, 6144, 9216), (5, 2080, 1024),
