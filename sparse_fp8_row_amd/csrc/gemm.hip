@@ -1606,10 +1606,10 @@ template <int XF, int WF, int OUT, int ACC, int RT>
 hipError_t run_decode_unit(const LinearArgs& a, hipStream_t stream) {
   // the permuted activation loads above 8 rows on the shapes whose weight
   // stream is long enough to hide the permutation (measured on the Llama
-  // shapes at M = 16: 0.3-1.9 us faster at N >= 6144 or K >= 8192, 0.15 us
-  // slower at N = K = 4096)
+  // shapes at M = 16 with the two-half units: 0.2-0.7 us faster at
+  // N = 14336 or K = 14336, 0.19 us slower at N = 6144, K = 4096)
   if (a.m == 1) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_ONE_ROW>(a, stream);
-  if (a.m <= 8 || (a.n < 6144 && a.k < 8192)) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_DIRECT>(a, stream);
+  if (a.m <= 8 || (a.n < 8192 && a.k < 8192)) return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_DIRECT>(a, stream);
   return run_decode_unit_cfg<XF, WF, OUT, ACC, RT, XM_PERMUTED>(a, stream);
 }
 
