@@ -274,7 +274,7 @@ sfr_status sparse_fp8_scaled_linear(const uint8_t* xq, sfr_fp8_t x_dt, const flo
  * (no workgroup waits for another), so the redundant work grows with rows x
  * workgroups.  One launch is taken for 1 or 2 rows with k up to 4096, or up
  * to 16384 while n / 16 does not exceed the device's CU count; for 3 or 4
- * rows with k up to 4096 and n / 16 at most 1.5 x the CU count.  Other shapes
+ * rows with k up to 4096 and n / 16 at most the CU count.  Other shapes
  * take two launches (quantization, then the linear layer).  Both paths write
  * the same bytes.
  *
