@@ -72,10 +72,11 @@ def test_graph_fused_one_row(gpu):
     replay_matches(step, eager)
 
 
-@pytest.mark.parametrize("m,n", [(2, 14336), (4, 4096), (16, 14336)])
-def test_graph_dynamic_rows(gpu, m, n):
-    # 2 and 4 rows: one launch; 16: quantization and linear layer
-    case = sfr_inputs.Case("graph", 43, m, n, 4096, bias=True)
+@pytest.mark.parametrize("m,n,k", [(2, 14336, 4096), (4, 4096, 4096), (16, 14336, 4096), (16, 4096, 14336)])
+def test_graph_dynamic_rows(gpu, m, n, k):
+    # 2 and 4 rows: one launch; 16: quantization and linear layer (32 weight
+    # rows per workgroup at n = 14336, 14 wavefronts of one unit at k = 14336)
+    case = sfr_inputs.Case("graph", 43, m, n, k, bias=True)
     x = dev_bf16(sfr_inputs.draw_x(case))
     pw = gpu.prepare_weight(dev_bf16(sfr_inputs.draw_w(case)))
     b = dev_bf16(sfr_inputs.draw_bias(case))
